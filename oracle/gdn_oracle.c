@@ -1,0 +1,250 @@
+/*
+ * gdn_oracle.c -- fp64 CPU oracle for the gated delta rule and the GDN mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header, table or helper with the HIP path.
+ *
+ * What it computes (the plain definition, token by token, in fp64):
+ *
+ *   Gated delta rule -- the recurrent linear-attention computation of the
+ *   Gated DeltaNet layers ("open-jev-fast" README, "Phase 3" item 1, which
+ *   cites Yang, Kautz & Hatamizadeh, "Gated Delta Networks", ICLR 2025; the
+ *   System1-Omni PR #186 page, "Purpose and summary", calls it the model's
+ *   recurrent linear-attention computation):
+ *
+ *       S_t = exp(g_t) * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *       o_t = S_t q_t
+ *
+ *   S_t is dv x dk.  The decay is applied first, then the delta correction
+ *   acts on the decayed state:  S <- e^g S;  S <- S + beta (v - S k) k^T.
+ *   This is the same expression multiplied out.
+ *
+ *   Packed variable-length batches: sequence n owns tokens
+ *   [cu[n], cu[n+1]) and has its own initial state h0[n] (prefix
+ *   continuation, "open-jev-fast" README, "Phase 2" item 2; PR #186,
+ *   "Review scope and map", per-candidate state).  h0 / hT are stored
+ *   key-major, H = S^T with shape [dk][dv].  A NULL h0 means a zero state.
+ *
+ *   Grouped value heads: v-head h reads q/k head h / (Hv/Hk)
+ *   ("open-jev-fast" README, "Phase 3" item 3: q/k at 16 heads).
+ *
+ *   Mixer ("open-jev-fast" README, "Phase 2" item 1: GDN input prep and the
+ *   gated RMSNorm):
+ *       c[t,ch] = sum_{j=0..3} w[ch,j] x[t-3+j,ch]   (zero before a sequence start)
+ *       a = c * sigmoid(c)
+ *       q,k per head:  x / sqrt(sum x^2 + eps_l2)
+ *       o = gated delta rule(q, k, v, g, beta)
+ *       y = o / sqrt(mean(o^2) + eps_norm) * w_norm * z * sigmoid(z)
+ *
+ * Precision: every value is fp64; inputs arrive already upcast to fp64.
+ * Threads: OpenMP over independent (sequence, v-head) pairs only; the
+ * arithmetic inside a pair is in token order, so results do not depend on
+ * the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* One (sequence, v-head) pair: the token recurrence written out. */
+static void recur_one(int64_t t_begin, int64_t t_end, int32_t Hk, int32_t Hv, int32_t dk,
+                      int32_t dv, int32_t h, const double *q, const double *k,
+                      const double *v, const double *g, const double *beta,
+                      const double *h0_nh, /* [dk][dv] or NULL */
+                      double *o, double *hT_nh /* [dk][dv] or NULL */, double *S,
+                      double *u) {
+  const int32_t group = Hv / Hk;
+  const int32_t hk = h / group;
+  /* S is dv x dk; h0 is stored key-major (H = S^T). */
+  for (int32_t i = 0; i < dv; ++i)
+    for (int32_t j = 0; j < dk; ++j)
+      S[(int64_t)i * dk + j] = h0_nh ? h0_nh[(int64_t)j * dv + i] : 0.0;
+
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const double *kt = k + (t * Hk + hk) * dk;
+    const double *qt = q + (t * Hk + hk) * dk;
+    const double *vt = v + (t * Hv + h) * dv;
+    const double gt = g[t * Hv + h];
+    const double bt = beta[t * Hv + h];
+    const double decay = exp(gt);
+    /* S <- exp(g_t) S */
+    for (int64_t e = 0; e < (int64_t)dv * dk; ++e) S[e] *= decay;
+    /* u = beta_t (v_t - S k_t) */
+    for (int32_t i = 0; i < dv; ++i) {
+      double sk = 0.0;
+      for (int32_t j = 0; j < dk; ++j) sk += S[(int64_t)i * dk + j] * kt[j];
+      u[i] = bt * (vt[i] - sk);
+    }
+    /* S <- S + u k_t^T */
+    for (int32_t i = 0; i < dv; ++i)
+      for (int32_t j = 0; j < dk; ++j) S[(int64_t)i * dk + j] += u[i] * kt[j];
+    /* o_t = S q_t */
+    double *ot = o + (t * Hv + h) * dv;
+    for (int32_t i = 0; i < dv; ++i) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * qt[j];
+      ot[i] = acc;
+    }
+  }
+  if (hT_nh)
+    for (int32_t i = 0; i < dv; ++i)
+      for (int32_t j = 0; j < dk; ++j) hT_nh[(int64_t)j * dv + i] = S[(int64_t)i * dk + j];
+}
+
+/*
+ * Gated delta rule over a packed batch.
+ *   q, k  : [T, Hk, dk]     v : [T, Hv, dv]     g, beta : [T, Hv]
+ *   cu    : [N+1], cu[0] = 0, non-decreasing, cu[N] = T
+ *   h0    : [N, Hv, dk, dv] or NULL;  hT : [N, Hv, dk, dv] or NULL
+ *   o     : [T, Hv, dv]
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_gdn_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                   const double *q, const double *k, const double *v, const double *g,
+                   const double *beta, const int64_t *cu, const double *h0, double *o,
+                   double *hT, int32_t nthreads) {
+  if (N < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || dk < 1 || dv < 1 || T < 0) return -1;
+  if (cu[0] != 0 || cu[N] != T) return -1;
+  for (int32_t n = 0; n < N; ++n)
+    if (cu[n + 1] < cu[n]) return -1;
+  const int64_t pairs = (int64_t)N * Hv;
+  const int64_t state = (int64_t)dk * dv;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double *S = (double *)malloc(sizeof(double) * state);
+    double *u = (double *)malloc(sizeof(double) * dv);
+    if (!S || !u) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      bad = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+      for (int64_t p = 0; p < pairs; ++p) {
+        const int32_t n = (int32_t)(p / Hv), h = (int32_t)(p % Hv);
+        const double *h0_nh = h0 ? h0 + ((int64_t)n * Hv + h) * state : NULL;
+        double *hT_nh = hT ? hT + ((int64_t)n * Hv + h) * state : NULL;
+        recur_one(cu[n], cu[n + 1], Hk, Hv, dk, dv, h, q, k, v, g, beta, h0_nh, o, hT_nh, S,
+                  u);
+      }
+    }
+    free(S);
+    free(u);
+  }
+  (void)nthreads;
+  return bad ? -2 : 0;
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/*
+ * Causal depthwise conv1d + SiLU over a packed batch (the first part of the
+ * GDN input prep).  x : [T, C];  w : [C, taps], tap taps-1 multiplies the
+ * current token; the window never reaches across a sequence start.
+ * out : [T, C].
+ */
+int oracle_conv_silu(int64_t T, int32_t N, int32_t C, int32_t taps, const double *x,
+                     const double *w, const int64_t *cu, double *out, int32_t nthreads) {
+  if (cu[0] != 0 || cu[N] != T) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+  for (int32_t ch = 0; ch < C; ++ch) {
+    for (int32_t n = 0; n < N; ++n) {
+      for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
+        double c = 0.0;
+        for (int32_t j = 0; j < taps; ++j) {
+          const int64_t src = t - (taps - 1) + j;
+          if (src >= cu[n]) c += w[(int64_t)ch * taps + j] * x[src * C + ch];
+        }
+        out[t * C + ch] = c * sigmoid(c);
+      }
+    }
+  }
+  (void)nthreads;
+  return 0;
+}
+
+/*
+ * Full mixer: conv+SiLU on all 2*Hk*dk + Hv*dv channels (q | k | v, head-major
+ * inside each), L2 norm of q and k per head, the gated delta rule, then the
+ * SiLU(z)-gated RMSNorm per (token, v-head) with a weight shared by all heads.
+ *   qkv [T, 2*Hk*dk + Hv*dv], conv_w [2*Hk*dk + Hv*dv, taps], g/beta [T, Hv],
+ *   z [T, Hv, dv], norm_w [dv], h0 [N, Hv, dk, dv] or NULL
+ *   -> y [T, Hv, dv], hT [N, Hv, dk, dv] or NULL.
+ * Intermediates (q, k, v after prep; o) are fp64 throughout.
+ */
+int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                     int32_t taps, double eps_l2, double eps_norm, const double *qkv,
+                     const double *conv_w, const double *g, const double *beta,
+                     const double *z, const double *norm_w, const int64_t *cu,
+                     const double *h0, double *y, double *hT, int32_t nthreads) {
+  const int32_t Cq = Hk * dk, Cv = Hv * dv, C = 2 * Cq + Cv;
+  const int64_t Tn = T > 0 ? T : 1;
+  double *a = (double *)malloc(sizeof(double) * Tn * C);
+  double *q = (double *)malloc(sizeof(double) * Tn * Cq);
+  double *k = (double *)malloc(sizeof(double) * Tn * Cq);
+  double *v = (double *)malloc(sizeof(double) * Tn * Cv);
+  double *o = (double *)malloc(sizeof(double) * Tn * Cv);
+  int rc = -2;
+  if (!a || !q || !k || !v || !o) goto done;
+  rc = oracle_conv_silu(T, N, C, taps, qkv, conv_w, cu, a, nthreads);
+  if (rc) goto done;
+  for (int64_t t = 0; t < T; ++t) {
+    const double *row = a + t * C;
+    for (int32_t hh = 0; hh < Hk; ++hh) {
+      const double *qs = row + (int64_t)hh * dk;
+      const double *ks = row + Cq + (int64_t)hh * dk;
+      double sq = 0.0, sk = 0.0;
+      for (int32_t j = 0; j < dk; ++j) {
+        sq += qs[j] * qs[j];
+        sk += ks[j] * ks[j];
+      }
+      const double rq = 1.0 / sqrt(sq + eps_l2), rk = 1.0 / sqrt(sk + eps_l2);
+      for (int32_t j = 0; j < dk; ++j) {
+        q[(t * Hk + hh) * dk + j] = qs[j] * rq;
+        k[(t * Hk + hh) * dk + j] = ks[j] * rk;
+      }
+    }
+    memcpy(v + t * Cv, row + 2 * Cq, sizeof(double) * Cv);
+  }
+  rc = oracle_gdn_fwd(T, N, Hk, Hv, dk, dv, q, k, v, g, beta, cu, h0, o, hT, nthreads);
+  if (rc) goto done;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < Hv; ++h) {
+      const double *os = o + (t * Hv + h) * dv;
+      const double *zs = z + (t * Hv + h) * dv;
+      double ms = 0.0;
+      for (int32_t j = 0; j < dv; ++j) ms += os[j] * os[j];
+      const double r = 1.0 / sqrt(ms / dv + eps_norm);
+      for (int32_t j = 0; j < dv; ++j)
+        y[(t * Hv + h) * dv + j] = os[j] * r * norm_w[j] * zs[j] * sigmoid(zs[j]);
+    }
+  }
+done:
+  free(a);
+  free(q);
+  free(k);
+  free(v);
+  free(o);
+  return rc;
+}
