@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked Gated DeltaNet prefill forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one gdn_chunk_fwd over one batch of synthetic inputs already resident in HBM (for the
+mixer workload: 48 back-to-back gdn_mixer_fwd layers).  Prints ONE JSON line with tokens/s per
+layer, the roofline of the dominant kernel (timed with HIP events on the launch stream, in a
+separate stage-by-stage loop), the whole-path roofline, and the fp64 CPU oracle timed on the host
+as a baseline.
+
+Workloads (seeded, synthetic; see gdn_inputs.py):
+    t539_h16x32      single sequence, T=539, Hk=16, Hv=32, d=128  (default)
+    t256_h4, varlen7_t677_h0, t3399_h16x32, t16384_h16x32
+    mixer_t936_x48   48 GDN mixer layers at T=936, Hk=16, Hv=32, one layer per seed
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+REC_BYTES, KC_BYTES = 18944, 16384   # per-(chunk, v-head) and per-(chunk, k-head) workspace records
+D = 128
+
+
+# ------------------------------------------------------------------------------------------------
+# Algorithmic bytes and flops
+# ------------------------------------------------------------------------------------------------
+def n_chunks(cu):
+    L = np.diff(np.asarray(cu, dtype=np.int64))
+    return int(np.sum((L + 63) // 64))
+
+
+def path_bytes(T, N, Hk, Hv, with_h0):
+    """Minimum HBM I/O of one gdn_chunk_fwd: q,k,v,g,beta in, o out, h0 in (if any), hT out."""
+    state = N * Hv * D * D * 4
+    return T * (2 * Hk * D * 2 + Hv * D * 2 + Hv * 8 + Hv * D * 2) + state * (2 if with_h0 else 1)
+
+
+def path_flops(T, Hk, Hv):
+    """Useful flops per token per v-head: three 128x128 products (W H, K^T U~, Q H) 98,304,
+    triangular 64-wide products 24,960, the 64x64 solve 2,731, K K^T + Q K^T 16,384 per k-head."""
+    r = Hv // Hk
+    return T * Hv * (98304 + 24960 + 2731 + 16384 / r)
+
+
+def prep_bytes(T, Hk, Hv, nch):
+    return T * Hk * D * 2 * 2 + T * Hv * 8 + nch * (Hv * REC_BYTES + Hk * KC_BYTES)
+
+
+def pass_bytes(T, N, Hk, Hv, nch, with_h0):
+    state = N * Hv * D * D * 4
+    return (T * Hk * D * 2 * 2 + T * Hv * D * 2 + nch * (Hv * REC_BYTES + Hk * KC_BYTES)
+            + T * Hv * D * 2 + state * (2 if with_h0 else 1))
+
+
+def mixer_bytes(T, N, Hk, Hv):
+    C = (2 * Hk + Hv) * D
+    return T * C * 2 + C * 4 * 2 + T * Hv * 8 + T * Hv * D * 2 * 2 + D * 2 + N * Hv * D * D * 4
+
+
+# ------------------------------------------------------------------------------------------------
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="t539_h16x32")
+    ap.add_argument("--rotate-mib", type=float, default=512.0,
+                    help="rotate among input copies until their footprint exceeds this (cold caches)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on oracle time for the baseline")
+    ap.add_argument("--copy-mib", type=float, default=0.0,
+                    help="also run a plain device copy of this size (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_chunked_amd as gdn
+    import gdn_inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} CUs={props.multi_processor_count} workload={args.workload}")
+
+    mixer = args.workload.startswith("mixer")
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    if not mixer:
+        case = gi.CASES[args.workload]
+        x = gi.make_case(args.workload)
+        T, N, Hk, Hv = case.T, case.N, case.Hk, case.Hv
+        with_h0 = x.h0 is not None
+        cu_host = torch.from_numpy(x.cu.astype(np.int64))
+        base = dict(q=bf(x.q), k=bf(x.k), v=bf(x.v), g=f32(x.g), beta=f32(x.beta),
+                    cu=torch.from_numpy(x.cu).to(dev), h0=None if x.h0 is None else f32(x.h0))
+        per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None) + \
+            T * Hv * D * 2 + N * Hv * D * D * 4
+        R = max(1, int(np.ceil(args.rotate_mib * 2 ** 20 / per_set)))
+        ws = torch.empty(gdn.gdn_chunk_fwd_workspace_size(T, N, Hk, Hv), dtype=torch.uint8, device=dev)
+        plans = []
+        for r in range(R):
+            s = base if r == 0 else {kk: (None if t is None else t.clone()) for kk, t in base.items()}
+            plans.append(gdn.ChunkPlan(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], s["h0"],
+                                       workspace=ws, cu_seqlens_host=cu_host))
+        step = lambda i: plans[i % R].forward()
+        tokens_per_step = T
+        layers_per_step = 1
+    else:
+        T, N, Hk, Hv, LAYERS = gi.MIXER_T, 1, 16, 32, gi.MIXER_LAYERS
+        with_h0 = False
+        log(f"[bench] generating {LAYERS} mixer layers")
+        layers = []
+        for l in range(LAYERS):
+            m = gi.make_mixer_inputs(100 + l)
+            layers.append(dict(qkv=bf(m.qkv), conv_w=bf(m.conv_w), g=f32(m.g), beta=f32(m.beta), z=bf(m.z),
+                               norm_w=bf(m.norm_w), cu=torch.from_numpy(m.cu).to(dev)))
+        cu_host = torch.tensor([0, T], dtype=torch.int64)
+        ws = torch.empty(gdn.gdn_mixer_fwd_workspace_size(T, N, Hk, Hv), dtype=torch.uint8, device=dev)
+        ys = [torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
+        hs = [torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+        R = 1
+
+        def step(i):
+            for l, L_ in enumerate(layers):
+                gdn.gdn_mixer_fwd(L_["qkv"], L_["conv_w"], L_["g"], L_["beta"], L_["z"], L_["norm_w"], L_["cu"],
+                                  None, y=ys[l], hT=hs[l], workspace=ws, cu_seqlens_host=cu_host)
+        tokens_per_step = T * LAYERS
+        layers_per_step = LAYERS
+
+    # ---- warmup + timed region ----------------------------------------------------------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = tokens_per_step / (ms_per_step * 1e-3)   # tokens per second per layer
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_s * 1e6 / args.steps:.1f} us)")
+
+    # ---- per-kernel timing (HIP events on the launch stream, one stage at a time) ---------------
+    stages = {}
+    if not mixer:
+        nch = n_chunks(x.cu)
+        dur = {"chunk_prep": [], "state_pass": []}
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+        for i in range(args.steps):
+            p = plans[i % R]
+            ev[3 * i].record()
+            p.prep()
+            ev[3 * i + 1].record()
+            p.state_pass()
+            ev[3 * i + 2].record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            dur["chunk_prep"].append(ev[3 * i].elapsed_time(ev[3 * i + 1]) * 1e3)
+            dur["state_pass"].append(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) * 1e3)
+        kbytes = {"chunk_prep": prep_bytes(T, Hk, Hv, nch), "state_pass": pass_bytes(T, N, Hk, Hv, nch, with_h0)}
+        for kname, ds in dur.items():
+            us = statistics.mean(ds)
+            stages[kname] = {"us_mean": us, "us_median": statistics.median(ds), "bytes": kbytes[kname],
+                             "GBps": kbytes[kname] / (us * 1e-6) / 1e9}
+            log(f"[bench] {kname}: {us:.2f} us mean, {stages[kname]['GBps']:.0f} GB/s of its own I/O")
+        dominant = max(stages, key=lambda k: stages[k]["us_mean"])
+        dom = stages[dominant]
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "bytes_per_launch": dom["bytes"], "us_per_launch": round(dom["us_mean"], 3)}
+        pb, pf = path_bytes(T, N, Hk, Hv, with_h0), path_flops(T, Hk, Hv)
+    else:
+        pb = layers_per_step * (mixer_bytes(T, N, Hk, Hv))
+        pf = layers_per_step * (path_flops(T, Hk, Hv) + T * (2 * Hk + Hv) * D * 8)
+        roofline = {"bound": "hbm", "kernel": "mixer step (48 layers)", "achieved": round(pb / (ms_per_step * 1e-3) / 1e9, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(pb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+    t_roof_us = max(pb / (HBM_PEAK_GBS * 1e9), pf / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    path = {"bytes": int(pb), "flops": int(pf), "t_roof_us": round(t_roof_us, 3),
+            "frac": round(t_roof_us / (ms_per_step * 1e3), 4),
+            "mfma_util_useful": round(pf / (ms_per_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+
+    # ---- parity of the timed outputs against the oracle (cheap for the default workload) ------
+    parity = None
+    if not mixer and T <= 4096:
+        import oracle
+        p = plans[(args.warmup + args.steps - 1) % R]
+        o_ref, h_ref = oracle.gdn_fwd(*x.f64())
+        o = p.o.float().cpu().numpy()
+        h = p.hT.cpu().numpy()
+        parity = {"o_rel_l2": float(np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)),
+                  "o_max_abs": float(np.abs(o - o_ref).max()),
+                  "hT_rel_l2": float(np.linalg.norm(h - h_ref) / np.linalg.norm(h_ref))}
+
+    # ---- optional plain copy kernel of known size (counter calibration) ----------------------
+    if args.copy_mib > 0:
+        n = int(args.copy_mib * 2 ** 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy kernel: {args.copy_mib} MiB read + {args.copy_mib} MiB written, 3 launches")
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload -----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.max_threads()
+        if not mixer:
+            f64 = x.f64()
+            t0 = time.perf_counter()
+            oracle.gdn_fwd(*f64)
+            once = time.perf_counter() - t0
+            reps = max(1, min(5, int(args.cpu_seconds / max(once, 1e-6))))
+            times = [once]
+            for _ in range(reps - 1):
+                t0 = time.perf_counter()
+                oracle.gdn_fwd(*f64)
+                times.append(time.perf_counter() - t0)
+            med = statistics.median(times)
+            cpu = {"value": round(T / med, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                   "sample": f"whole workload ({T} tokens, {Hv} v-heads), median of {len(times)} runs, fp64"}
+        else:
+            m = gi.make_mixer_inputs(100)
+            fb = gi.bits_to_f64
+            t0 = time.perf_counter()
+            oracle.mixer_fwd(fb(m.qkv), fb(m.conv_w), m.g, m.beta, fb(m.z), fb(m.norm_w), m.cu, None)
+            once = time.perf_counter() - t0
+            cpu = {"value": round(T / once, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                   "sample": f"one of the 48 layers ({T} tokens), fp64"}
+        log(f"[bench] cpu baseline {cpu['value']} tokens/s on {threads} threads")
+
+    cfg = {"workload": args.workload, "T": T, "N": N, "Hk": Hk, "Hv": Hv, "d": D, "chunk": 64,
+           "rotating_input_sets": R, "layers_per_step": layers_per_step}
+    line = {"metric": "GDN prefill tokens/s per layer (Hk16/Hv32,d128) + % MFMA/HBM roofline",
+            "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg,
+            "roofline": roofline, "cpu_baseline": cpu, "path_roofline": path, "stages": stages,
+            "parity": parity, "device": {"name": props.name, "cus": props.multi_processor_count}}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,266 @@
+"""Python binding of libgdn -- chunked Gated DeltaNet prefill forward on AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind the C ABI
+declared in ``include/gdn.h``.  PyTorch supplies device memory and the stream; there is no CPU or
+PyTorch fallback.  If ``libgdn.so`` has not been built, every entry point raises.
+
+Entry points (same names as the C ABI):
+    gdn_abi_version(), gdn_status_string(code), gdn_last_hip_error()
+    gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
+    gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, hT)
+    gdn_chunk_prep / gdn_state_pass: the two stages of gdn_chunk_fwd (see ChunkPlan)
+    gdn_mixer_fwd_workspace_size(T, N, Hk, Hv)
+    gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, ...) -> (y, hT)
+
+Layouts (row-major, contiguous): q, k bf16 [T, Hk, 128]; v bf16 [T, Hv, 128]; g, beta fp32
+[T, Hv]; cu_seqlens int32 [N+1]; h0, hT fp32 [N, Hv, 128, 128] key-major (H = S^T); o bf16
+[T, Hv, 128].  See ``include/gdn.h`` for the full contract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+D = 128
+
+GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED = 0, 1, 2, 3
+GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_ALIAS, GDN_ERR_HIP = 4, 5, 6, 7
+
+EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_last_hip_error",
+                    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prep", "gdn_state_pass",
+                    "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd")
+
+
+class ChunkDesc(ctypes.Structure):
+    _fields_ = [("total_tokens", ctypes.c_int64), ("num_seqs", ctypes.c_int32),
+                ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class MixerDesc(ctypes.Structure):
+    _fields_ = [("chunk", ChunkDesc), ("conv_taps", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = f"{where}: {gdn_status_string(code)}"
+        if code == GDN_ERR_HIP:
+            msg += f" (hipError {gdn_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_deltanet_chunked_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_last_hip_error.restype = ctypes.c_int
+        L.gdn_chunk_fwd_workspace_size.restype = S
+        L.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.gdn_chunk_fwd.restype = ctypes.c_int
+        L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 10
+        L.gdn_chunk_prep.restype = ctypes.c_int
+        L.gdn_chunk_prep.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 6
+        L.gdn_state_pass.restype = ctypes.c_int
+        L.gdn_state_pass.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 8
+        L.gdn_mixer_fwd_workspace_size.restype = S
+        L.gdn_mixer_fwd_workspace_size.argtypes = [ctypes.POINTER(MixerDesc)]
+        L.gdn_mixer_fwd.restype = ctypes.c_int
+        L.gdn_mixer_fwd.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11
+        _lib_handle = L
+    return _lib_handle
+
+
+def gdn_abi_version() -> int:
+    return int(lib().gdn_abi_version())
+
+
+def gdn_status_string(code: int) -> str:
+    return lib().gdn_status_string(int(code)).decode()
+
+
+def gdn_last_hip_error() -> int:
+    return int(lib().gdn_last_hip_error())
+
+
+def _desc(T, N, Hk, Hv, ws=None, ws_bytes=0, dk=D, dv=D) -> ChunkDesc:
+    return ChunkDesc(int(T), int(N), int(Hk), int(Hv), int(dk), int(dv), ws, int(ws_bytes))
+
+
+def gdn_chunk_fwd_workspace_size(T: int, N: int, Hk: int, Hv: int) -> int:
+    return int(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(_desc(T, N, Hk, Hv))))
+
+
+def gdn_mixer_fwd_workspace_size(T: int, N: int, Hk: int, Hv: int, conv_taps: int = 4,
+                                 norm_eps: float = 1e-6) -> int:
+    m = MixerDesc(_desc(T, N, Hk, Hv), conv_taps, norm_eps)
+    return int(lib().gdn_mixer_fwd_workspace_size(ctypes.byref(m)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _check_cu(cu_seqlens, T, cu_host):
+    host = cu_host if cu_host is not None else cu_seqlens.detach().cpu()
+    host = torch.as_tensor(host).to(torch.int64)
+    if host.ndim != 1 or host.numel() < 2 or int(host[0]) != 0 or int(host[-1]) != T or bool((host[1:] < host[:-1]).any()):
+        raise ValueError("cu_seqlens must be non-decreasing, start at 0 and end at T")
+    return host.numel() - 1
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, want_state=True,
+                  workspace=None, stream=None, cu_seqlens_host=None):
+    """Chunked gated-delta-rule forward.  Returns (o, hT) (hT is None if not wanted).
+
+    ``cu_seqlens_host`` (a CPU copy) avoids the device sync of checking ``cu_seqlens``.
+    ``workspace`` (uint8 CUDA tensor) may be passed to avoid an allocation per call.
+    """
+    dev = q.device
+    T, Hk = int(q.shape[0]), int(q.shape[1])
+    Hv = int(v.shape[1])
+    _check(q, "q", torch.bfloat16, (T, Hk, D), dev)
+    _check(k, "k", torch.bfloat16, (T, Hk, D), dev)
+    _check(v, "v", torch.bfloat16, (T, Hv, D), dev)
+    _check(g, "g", torch.float32, (T, Hv), dev)
+    _check(beta, "beta", torch.float32, (T, Hv), dev)
+    N = _check_cu(cu_seqlens, T, cu_seqlens_host)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
+    if o is None:
+        o = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
+    _check(o, "o", torch.bfloat16, (T, Hv, D), dev)
+    if hT is None and want_state:
+        hT = torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+    if hT is not None:
+        _check(hT, "hT", torch.float32, (N, Hv, D, D), dev)
+    need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
+    if need == 0:
+        raise GdnError(GDN_ERR_SHAPE, "gdn_chunk_fwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    d = _desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel())
+    rc = lib().gdn_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                             _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd")
+    return o, hT
+
+
+class ChunkPlan:
+    """Checked arguments of one gdn_chunk_fwd shape, for calling the two stages separately
+    (gdn_chunk_prep then gdn_state_pass) -- e.g. to time each kernel on its own."""
+
+    def __init__(self, q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, workspace=None,
+                 cu_seqlens_host=None):
+        dev = q.device
+        T, Hk, Hv = int(q.shape[0]), int(q.shape[1]), int(v.shape[1])
+        _check(q, "q", torch.bfloat16, (T, Hk, D), dev)
+        _check(k, "k", torch.bfloat16, (T, Hk, D), dev)
+        _check(v, "v", torch.bfloat16, (T, Hv, D), dev)
+        _check(g, "g", torch.float32, (T, Hv), dev)
+        _check(beta, "beta", torch.float32, (T, Hv), dev)
+        N = _check_cu(cu_seqlens, T, cu_seqlens_host)
+        _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+        if h0 is not None:
+            _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
+        self.o = o if o is not None else torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
+        self.hT = hT if hT is not None else torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+        _check(self.o, "o", torch.bfloat16, (T, Hv, D), dev)
+        _check(self.hT, "hT", torch.float32, (N, Hv, D, D), dev)
+        need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
+        self.workspace = workspace if workspace is not None and workspace.numel() >= need else \
+            torch.empty(need, dtype=torch.uint8, device=dev)
+        self.desc = _desc(T, N, Hk, Hv, self.workspace.data_ptr(), self.workspace.numel())
+        self.args = (q, k, v, g, beta, cu_seqlens, h0)
+
+    def prep(self, stream=None):
+        q, k, v, g, beta, cu, h0 = self.args
+        rc = lib().gdn_chunk_prep(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu),
+                                  _stream(stream))
+        if rc != GDN_OK:
+            raise GdnError(rc, "gdn_chunk_prep")
+
+    def state_pass(self, stream=None):
+        q, k, v, g, beta, cu, h0 = self.args
+        rc = lib().gdn_state_pass(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(h0),
+                                  _ptr(self.o), _ptr(self.hT), _stream(stream))
+        if rc != GDN_OK:
+            raise GdnError(rc, "gdn_state_pass")
+
+    def forward(self, stream=None):
+        q, k, v, g, beta, cu, h0 = self.args
+        rc = lib().gdn_chunk_fwd(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu),
+                                 _ptr(h0), _ptr(self.o), _ptr(self.hT), _stream(stream))
+        if rc != GDN_OK:
+            raise GdnError(rc, "gdn_chunk_fwd")
+
+
+def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16, Hv=32, y=None, hT=None,
+                  want_state=True, norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
+    """GDN mixer forward (conv + SiLU + L2 norm, the chunked rule, gated RMSNorm).  Returns (y, hT)."""
+    dev = qkv.device
+    T = int(qkv.shape[0])
+    C = (2 * Hk + Hv) * D
+    _check(qkv, "qkv", torch.bfloat16, (T, C), dev)
+    _check(conv_w, "conv_w", torch.bfloat16, (C, 4), dev)
+    _check(g, "g", torch.float32, (T, Hv), dev)
+    _check(beta, "beta", torch.float32, (T, Hv), dev)
+    _check(z, "z", torch.bfloat16, (T, Hv, D), dev)
+    _check(norm_w, "norm_w", torch.bfloat16, (D,), dev)
+    N = _check_cu(cu_seqlens, T, cu_seqlens_host)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
+    if y is None:
+        y = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
+    _check(y, "y", torch.bfloat16, (T, Hv, D), dev)
+    if hT is None and want_state:
+        hT = torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+    if hT is not None:
+        _check(hT, "hT", torch.float32, (N, Hv, D, D), dev)
+    need = gdn_mixer_fwd_workspace_size(T, N, Hk, Hv, 4, norm_eps)
+    if need == 0:
+        raise GdnError(GDN_ERR_SHAPE, "gdn_mixer_fwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    m = MixerDesc(_desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), 4, float(norm_eps))
+    rc = lib().gdn_mixer_fwd(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
+                             _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_mixer_fwd")
+    return y, hT

@@ -1,0 +1,108 @@
+// gdn_device.h -- device-side helpers shared by the libgdn HIP kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions (v_mfma_f32_16x16x32_bf16, wave64):
+//   A operand (16 x 32):  lane l holds row (l % 16), 8 consecutive k values of k-group (l / 16)
+//   B operand (32 x 16):  lane l holds column (l % 16), the 8 k values of k-group (l / 16)
+//   C/D (16 x 16, fp32):  lane l holds column (l % 16), rows 4*(l / 16) + r, r = 0..3
+// Element e of lane group g in A multiplies element e of lane group g in B, so any consistent
+// assignment of contraction indices to (g, e) slots gives the same product; the kernels use that
+// freedom to feed accumulators back as operands without moving data between lanes.
+// v_mfma_f32_16x16x4_f32 has the same C/D layout; A lane l holds A[l % 16][k = l / 16] and B lane l
+// holds B[k = l / 16][l % 16].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kDim = 128;    // dk = dv
+constexpr int kDvTile = 16;  // value columns per state-pass workgroup
+constexpr int kDvTiles = kDim / kDvTile;
+
+// ---- per-(chunk slot, v-head) record written by the prep kernel, read by the state pass ----
+// Six 16x32 A-operand fragments cover the lower block triangle of a 64x64 chunk matrix:
+//   fragment f -> (row block, k step): 0:(0,0) 1:(1,0) 2:(2,0) 3:(2,1) 4:(3,0) 5:(3,1)
+// Row block w therefore owns fragments kFragBase[w] .. kFragBase[w] + kFragCount[w] - 1.
+constexpr int kFrags = 6;
+constexpr int kFragBytes = 64 * 16;                       // 64 lanes x 8 bf16
+constexpr int kRecTpHi = 0;                               // T' = (I+A)^-1 diag(beta), bf16 high part
+constexpr int kRecTpLo = kRecTpHi + kFrags * kFragBytes;  // T' low part (T' - hi rounded to bf16)
+constexpr int kRecP = kRecTpLo + kFrags * kFragBytes;     // P = tril(Q K^T o e^{G_i - G_j}), bf16
+constexpr int kRecEG = kRecP + kFrags * kFragBytes;       // e^{G_i}           fp32[64]
+constexpr int kRecED = kRecEG + kChunk * 4;               // e^{G_last - G_i}  fp32[64]
+constexpr int kRecBytes = kRecED + kChunk * 4;            // 18944
+// ---- per-(chunk slot, k-head) record: K^T as 16 A-operand fragments (dk block rb, token step ks)
+constexpr int kKcFrags = 16;                              // fragment rb * 2 + ks
+constexpr int kKcBytes = kKcFrags * kFragBytes;           // 16384
+
+__host__ __device__ constexpr int frag_row_block(int f) { return f < 2 ? f : (f < 4 ? 2 : 3); }
+__host__ __device__ constexpr int frag_k_step(int f) { return (f == 3 || f == 5) ? 1 : 0; }
+
+// Chunk-slot numbering: chunk c of sequence n lives in slot cu[n] / 64 + n + c.  The map is
+// injective and monotone, and every slot index is below T / 64 + N.
+__host__ __device__ inline int64_t num_slots(int64_t T, int32_t N) { return T / kChunk + N; }
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 round-to-nearest-even (hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+__device__ __forceinline__ float from_bf16(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float bits_to_float(unsigned short b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ unsigned short bf16_bits(__bf16 x) {
+  return __builtin_bit_cast(unsigned short, x);
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 significant bits in total.
+__device__ __forceinline__ void split_hilo(float x, __bf16 &hi, __bf16 &lo) {
+  hi = to_bf16(x);
+  lo = to_bf16(x - from_bf16(hi));
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// 16-byte global load of 8 bf16 (caller guarantees 16-byte alignment).
+__device__ __forceinline__ bf16x8 load_bf16x8(const void *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void store_bf16x8(void *p, bf16x8 x) {
+  *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, x);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (hardware id b runs on XCD b % 8).  Renumber
+// so that consecutive logical ids share an XCD and therefore its L2.
+__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
+  if (nblocks % 8 != 0) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}
+
+}  // namespace gdn

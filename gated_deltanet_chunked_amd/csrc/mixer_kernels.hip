@@ -1,0 +1,151 @@
+// mixer_kernels.hip -- the GDN layer's input prep and output norm around the chunked rule.
+//
+// The "open-jev-fast" README ("Phase 2", item 1) fuses the Gated DeltaNet input prep (causal
+// conv, SiLU, q/k/v split, L2 norm) into one kernel and the gated RMSNorm into another; "Phase 3"
+// item 3 computes q/k at the 16 key heads.  Both kernels here are HBM-bound streams: 16-byte
+// vector loads and stores, fp32 math, and the per-row reductions as 16-lane butterflies inside a
+// wave (no LDS).
+#include "gdn_device.h"
+
+namespace gdn {
+
+namespace {
+
+__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+
+__device__ __forceinline__ float sum16(float x) {
+  // butterfly over the 16 lanes that share l / 16
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Start token of the sequence that contains token t (cu is monotone, cu[0] = 0).
+__device__ __forceinline__ int seq_start(const int32_t *__restrict__ cu, int N, int t) {
+  int lo = 0, hi = N - 1;  // largest n with cu[n] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return cu[lo];
+}
+
+}  // namespace
+
+// Grid: (ceil(T / 64), 2 Hk + Hv).  Block y selects a 128-channel head segment of the packed
+// q | k | v channels; each thread owns 8 channels x 4 tokens.  Lanes 16m .. 16m+15 of a wave hold
+// the 16 channel groups of the same tokens, so the per-token L2 norm is a 16-lane butterfly.
+__global__ __launch_bounds__(256) void mixer_prep_kernel(
+    const unsigned short *__restrict__ qkv, const unsigned short *__restrict__ conv_w,
+    const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv,
+    unsigned short *__restrict__ qo, unsigned short *__restrict__ ko,
+    unsigned short *__restrict__ vo) {
+  const int seg = blockIdx.y;                  // 0..Hk-1: q heads, Hk..2Hk-1: k heads, then v heads
+  const int C = (2 * Hk + Hv) * kDim;
+  const int tid = threadIdx.x, chg = tid & 15, tg = tid >> 4;  // channel group, token group
+  const int ch0 = seg * kDim + chg * 8;
+  const bool is_qk = seg < 2 * Hk;
+
+  // conv weights of my 8 channels: w[ch][0..3], tap 3 multiplies the current token
+  float wt[8][4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+    const u16x4 wv = *reinterpret_cast<const u16x4 *>(conv_w + (size_t)(ch0 + e) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wt[e][j] = bits_to_float(wv[j]);
+  }
+
+  const int tbase = blockIdx.x * 64 + tg * 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = tbase + u;
+    const bool valid = t < T;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (valid) {
+      const int ss = seq_start(cu, N, t);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = t - 3 + j;
+        if (src >= ss) {
+          const u16x8 xv = *reinterpret_cast<const u16x8 *>(qkv + (size_t)src * C + ch0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += wt[e][j] * bits_to_float(xv[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = silu(acc[e]);
+    }
+    if (is_qk) {
+      float ss2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss2 += acc[e] * acc[e];
+      ss2 = sum16(ss2);
+      const float rn = 1.f / sqrtf(ss2 + 1e-6f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= rn;
+    }
+    if (valid) {
+      u16x8 out;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = bf16_bits(to_bf16(acc[e]));
+      unsigned short *dst;
+      if (seg < Hk) dst = qo + ((size_t)t * Hk + seg) * kDim;
+      else if (seg < 2 * Hk) dst = ko + ((size_t)t * Hk + (seg - Hk)) * kDim;
+      else dst = vo + ((size_t)t * Hv + (seg - 2 * Hk)) * kDim;
+      *reinterpret_cast<u16x8 *>(dst + chg * 8) = out;
+    }
+  }
+}
+
+// y = o / sqrt(mean(o^2) + eps) * w * z * sigmoid(z), one (token, v-head) row of 128 per 16 lanes.
+__global__ __launch_bounds__(256) void gated_rmsnorm_kernel(
+    const unsigned short *__restrict__ o, const unsigned short *__restrict__ z,
+    const unsigned short *__restrict__ norm_w, float eps, int64_t rows,
+    unsigned short *__restrict__ y) {
+  const int tid = threadIdx.x, chg = tid & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const bool valid = row < rows;
+  const size_t off = (size_t)(valid ? row : 0) * kDim + chg * 8;
+  const u16x8 ov = *reinterpret_cast<const u16x8 *>(o + off);
+  const u16x8 zv = *reinterpret_cast<const u16x8 *>(z + off);
+  const u16x8 wv = *reinterpret_cast<const u16x8 *>(norm_w + chg * 8);
+  float of[8], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    of[e] = bits_to_float(ov[e]);
+    ss += of[e] * of[e];
+  }
+  ss = sum16(ss);
+  const float r = 1.f / sqrtf(ss * (1.f / kDim) + eps);
+  u16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float zf = bits_to_float(zv[e]);
+    out[e] = bf16_bits(to_bf16(of[e] * r * bits_to_float(wv[e]) * silu(zf)));
+  }
+  if (valid) *reinterpret_cast<u16x8 *>(y + off) = out;
+}
+
+void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
+                       int Hk, int Hv, void *q, void *k, void *v, hipStream_t stream) {
+  dim3 grid((unsigned)((T + 63) / 64), (unsigned)(2 * Hk + Hv));
+  hipLaunchKernelGGL(mixer_prep_kernel, grid, dim3(256), 0, stream,
+                     static_cast<const unsigned short *>(qkv),
+                     static_cast<const unsigned short *>(conv_w), cu, (int)T, N, Hk, Hv,
+                     static_cast<unsigned short *>(q), static_cast<unsigned short *>(k),
+                     static_cast<unsigned short *>(v));
+}
+
+void launch_gated_rmsnorm(const void *o, const void *z, const void *norm_w, float eps, int64_t T,
+                          int Hv, void *y, hipStream_t stream) {
+  const int64_t rows = T * Hv;
+  hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
+                     static_cast<const unsigned short *>(o), static_cast<const unsigned short *>(z),
+                     static_cast<const unsigned short *>(norm_w), eps, rows,
+                     static_cast<unsigned short *>(y));
+}
+
+}  // namespace gdn

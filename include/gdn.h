@@ -1,0 +1,162 @@
+/*
+ * gdn.h -- libgdn: chunked Gated DeltaNet prefill forward for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the gated delta rule, the recurrent linear-attention computation of the
+ * Gated DeltaNet layers (System1-Omni PR #186 page, "Purpose and summary"; computed in 64-token
+ * chunks as the "open-jev-fast" README describes under "Phase 3", item 1, after the Gated
+ * DeltaNet paper it cites as reference [5]):
+ *
+ *     S_t = exp(g_t) * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * over packed variable-length sequences, each with its own optional fp32 initial state (the
+ * prefix-continuation form: the "open-jev-fast" README, "Phase 2" item 2, hands a prefix's final
+ * recurrent state to each candidate; PR #186, "Review scope and map", keeps per-candidate state).
+ * There is no 1/sqrt(dk) scale on q: o_t = S_t q_t exactly.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Every data pointer is DEVICE memory owned by the caller.  The library never allocates,
+ *    frees or synchronises, and keeps no state between calls except a per-thread copy of the
+ *    last HIP error.  All work is enqueued on the caller's `stream` (NULL = the default stream).
+ *  * Layouts are row-major and contiguous.  bf16 tensors are raw 16-bit bf16 values.
+ *      q, k    : bf16 [T, Hk, dk]          v : bf16 [T, Hv, dv]
+ *      g, beta : fp32 [T, Hv]   (g is the log-decay, one value per token per v-head)
+ *      cu_seqlens : int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = T
+ *      h0, hT  : fp32 [N, Hv, dk, dv], key-major: element [n][h][i][j] = S[j][i] (H = S^T)
+ *      o       : bf16 [T, Hv, dv]
+ *    v-head h reads q/k head h / (Hv / Hk) ("open-jev-fast" README, "Phase 3" item 3: q/k at 16
+ *    heads, v at 32).
+ *  * Alignment: bf16 tensors (q, k, v, o, qkv, z, norm_w, y), states (h0, hT) and the workspace
+ *    16 bytes; conv_w 8 bytes; g, beta and cu_seqlens 4 bytes (GDN_ERR_ALIGN otherwise).
+ *  * All argument checks happen on the host BEFORE anything is enqueued.  On any error nothing
+ *    is launched and the outputs are untouched.  GDN_OK means "enqueued": results are valid once
+ *    the stream reaches that point.  GDN_ERR_HIP means a launch failed; gdn_last_hip_error()
+ *    returns the hipError_t of the calling thread's last such failure.
+ *  * The library cannot read cu_seqlens without a device sync, so it trusts that they are
+ *    monotone with cu[N] = T (the Python binding checks a host copy).  Zero-length sequences are
+ *    allowed: they produce no output rows and hT[n] = h0[n] (or zeros).
+ *  * hT may be exactly h0 (in-place continuation).  Any other overlap of an output with an
+ *    input, or of o with hT, is GDN_ERR_ALIAS.
+ *  * The workspace is caller-owned device memory of at least *_workspace_size() bytes; its
+ *    contents on entry are ignored and on exit are unspecified.  Calls that share a workspace
+ *    must be ordered on one stream.
+ *  * Only dk = dv = 128 is supported (GDN_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef LIBGDN_GDN_H
+#define LIBGDN_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef GDN_EXPORT
+#define GDN_EXPORT __attribute__((visibility("default")))
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  GDN_ERR_SHAPE = 2,       /* N < 1, T < 0, Hk < 1, Hv % Hk != 0, or a size overflows       */
+  GDN_ERR_UNSUPPORTED = 3, /* dk or dv other than 128, or a conv/norm setting not supported  */
+  GDN_ERR_ALIGN = 4,       /* a pointer is not aligned as required                          */
+  GDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the required size              */
+  GDN_ERR_ALIAS = 6,       /* an output overlaps an input or the workspace (hT == h0 is ok) */
+  GDN_ERR_HIP = 7          /* a HIP launch failed; see gdn_last_hip_error()                 */
+} gdn_status;
+
+/* Problem description.  Sizes are host values; nothing is read from device memory. */
+typedef struct {
+  int64_t total_tokens;   /* T = cu_seqlens[N] (>= 0)                                     */
+  int32_t num_seqs;       /* N >= 1                                                       */
+  int32_t num_k_heads;    /* Hk >= 1 (q and k heads)                                      */
+  int32_t num_v_heads;    /* Hv, a multiple of Hk                                         */
+  int32_t head_dim_k;     /* dk, must be 128                                              */
+  int32_t head_dim_v;     /* dv, must be 128                                              */
+  void *workspace;        /* device, caller-owned, >= gdn_chunk_fwd_workspace_size() bytes */
+  size_t workspace_bytes;
+} gdn_chunk_desc;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION at build time). */
+GDN_EXPORT int gdn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+GDN_EXPORT const char *gdn_status_string(int status);
+
+/* hipError_t of the calling thread's last GDN_ERR_HIP, 0 if none. */
+GDN_EXPORT int gdn_last_hip_error(void);
+
+/* Workspace bytes gdn_chunk_fwd needs for this shape; 0 if the description is invalid.
+ * The workspace and pointer fields of *d are ignored. */
+GDN_EXPORT size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d);
+
+/*
+ * Chunked gated-delta-rule prefill forward over a packed batch.
+ *   q, k, v, g, beta, cu_seqlens : inputs as laid out above (device)
+ *   h0 : initial states, or NULL for zero states (device)
+ *   o  : output (device), written for every token
+ *   hT : final states, or NULL to skip them (device); may equal h0
+ * Computes in 64-token chunks: per chunk a local cumsum of g, the K K^T / (I + A)^-1 UT
+ * transform, a sequential inter-chunk state pass with fp32 state, and the chunk output
+ * ("open-jev-fast" README, "Phase 3" item 1, names these steps).
+ */
+GDN_EXPORT int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
+                  const float *g, const float *beta, const int32_t *cu_seqlens, const float *h0,
+                  void *o, float *hT, void *stream);
+
+/*
+ * The two stages of gdn_chunk_fwd, callable on their own (gdn_chunk_fwd = gdn_chunk_prep, then
+ * gdn_state_pass, on one stream with one workspace).  The "open-jev-fast" README ("Phase 3",
+ * item 1) separates the work that does not depend on the recurrent state, which runs for many
+ * chunks side by side, from the state that is passed chunk to chunk.
+ *
+ * gdn_chunk_prep: for every (chunk, k-head) in parallel -- local cumsum of g, K K^T and Q K^T,
+ *   A = beta_i e^{G_i - G_j} k_i.k_j (i > j), T = (I + A)^-1 -- writes T diag(beta), the masked
+ *   decayed Q K^T, the decays and K^T into the workspace.  Reads q, k, g, beta, cu_seqlens.
+ * gdn_state_pass: for every (sequence, v-head, 16 value columns) in parallel, walks the chunks
+ *   in order with the fp32 state on chip, writing o and hT.  Reads q, k, v, cu_seqlens, h0 and
+ *   the workspace exactly as gdn_chunk_prep left it for the same inputs and shapes.
+ * Arguments, layouts and errors are those of gdn_chunk_fwd.
+ */
+GDN_EXPORT int gdn_chunk_prep(const gdn_chunk_desc *d, const void *q, const void *k,
+                              const float *g, const float *beta, const int32_t *cu_seqlens,
+                              void *stream);
+GDN_EXPORT int gdn_state_pass(const gdn_chunk_desc *d, const void *q, const void *k,
+                              const void *v, const int32_t *cu_seqlens, const float *h0, void *o,
+                              float *hT, void *stream);
+
+/*
+ * GDN mixer: the gated delta rule with its input prep and output norm ("open-jev-fast" README,
+ * "Phase 2" item 1: causal conv, SiLU, q/k/v split, L2 norm; gated RMSNorm).
+ *   qkv    : bf16 [T, 2*Hk*dk + Hv*dv], channels q | k | v, head-major inside each block
+ *   conv_w : bf16 [2*Hk*dk + Hv*dv, conv_taps]; tap conv_taps-1 multiplies the current token;
+ *            the window holds zeros before every sequence start (no bias)
+ *   per channel: c = causal depthwise conv; a = c * sigmoid(c)
+ *   per (token, k-head): q, k = a / sqrt(sum a^2 + 1e-6)
+ *   o = gated delta rule(q, k, v = a, g, beta, h0) as gdn_chunk_fwd
+ *   y = o / sqrt(mean_dv(o^2) + norm_eps) * norm_w * z * sigmoid(z)   per (token, v-head)
+ *   z : bf16 [T, Hv, dv];  norm_w : bf16 [dv], shared by all heads;  y : bf16 [T, Hv, dv]
+ * Only conv_taps = 4 is supported.
+ */
+typedef struct {
+  gdn_chunk_desc chunk;   /* shapes and workspace (gdn_mixer_fwd_workspace_size bytes) */
+  int32_t conv_taps;      /* 4                                                          */
+  float norm_eps;         /* RMSNorm epsilon, e.g. 1e-6                                 */
+} gdn_mixer_desc;
+
+GDN_EXPORT size_t gdn_mixer_fwd_workspace_size(const gdn_mixer_desc *d);
+
+GDN_EXPORT int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
+                  const float *beta, const void *z, const void *norm_w,
+                  const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGDN_GDN_H */

@@ -52,8 +52,12 @@ def load_library(path: str):
     lib.oracle_gdn_fwd.restype = ctypes.c_int
     lib.oracle_conv_silu.argtypes = [i64, i32, i32, i32, P, P, P, P, i32]
     lib.oracle_conv_silu.restype = ctypes.c_int
-    lib.oracle_mixer_fwd.argtypes = [i64, i32, i32, i32, i32, i32, i32, f64, f64,
+    lib.oracle_mixer_fwd.argtypes = [i64, i32, i32, i32, i32, i32, i32, f64, f64, i32,
                                      P, P, P, P, P, P, P, P, P, P, i32]
+    lib.oracle_round_bf16.argtypes = [f64]
+    lib.oracle_round_bf16.restype = f64
+    lib.oracle_round_bf16_array.argtypes = [P, P, i64]
+    lib.oracle_round_bf16_array.restype = None
     lib.oracle_mixer_fwd.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -126,9 +130,20 @@ def conv_silu(x, w, cu_seqlens, threads: int = 0, lib=None):
     return out
 
 
+def round_bf16(x, lib=None):
+    """Round fp64 values to bf16 (8 significant bits, ties to even), elementwise."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(a)
+    (lib or _load()).oracle_round_bf16_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
 def mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, Hk=16, Hv=32, dk=128, dv=128,
-              eps_l2=1e-6, eps_norm=1e-6, threads: int = 0, lib=None):
-    """Full GDN mixer in fp64. Returns (y [T, Hv, dv], hT [N, Hv, dk, dv])."""
+              eps_l2=1e-6, eps_norm=1e-6, bf16_points: bool = True, threads: int = 0, lib=None):
+    """Full GDN mixer in fp64. Returns (y [T, Hv, dv], hT [N, Hv, dk, dv]).
+
+    bf16_points: round the prepped q, k, v and the rule's output o to bf16 where the bf16 model
+    does ("open-jev-fast" README, "Phase 2" item 1); all other arithmetic is fp64."""
     qkv, conv_w, g, beta, z, norm_w = (_f64(x) for x in (qkv, conv_w, g, beta, z, norm_w))
     T = qkv.shape[0]
     cu = _cu(cu_seqlens, T)
@@ -140,7 +155,7 @@ def mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, Hk=16, Hv=32
     y = np.zeros((T, Hv, dv))
     hT = np.zeros((N, Hv, dk, dv))
     rc = (lib or _load()).oracle_mixer_fwd(T, N, Hk, Hv, dk, dv, conv_w.shape[1], float(eps_l2), float(eps_norm),
-                                  _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
+                                  int(bool(bf16_points)), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
                                   _ptr(cu), _ptr(h0), _ptr(y), _ptr(hT), int(threads))
     if rc != 0:
         raise RuntimeError(f"oracle_mixer_fwd failed ({rc})")

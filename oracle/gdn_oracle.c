@@ -37,6 +37,11 @@
  *       o = gated delta rule(q, k, v, g, beta)
  *       y = o / sqrt(mean(o^2) + eps_norm) * w_norm * z * sigmoid(z)
  *
+ *   The model is bf16 and its fused prep / norm kernels keep the reference's bf16 rounding
+ *   points ("open-jev-fast" README, "Phase 2" item 1).  With bf16_points != 0 the mixer rounds
+ *   the prepped q, k, v and the rule's output o to bf16 (round to nearest, ties to even) at
+ *   exactly those points; every other value stays fp64.
+ *
  * Precision: every value is fp64; inputs arrive already upcast to fp64.
  * Threads: OpenMP over independent (sequence, v-head) pairs only; the
  * arithmetic inside a pair is in token order, so results do not depend on
@@ -155,6 +160,23 @@ int oracle_gdn_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
+/* Round to the nearest value with 8 significant bits (bf16), ties to even.  Finite inputs in
+ * bf16's normal range (|x| >= 2^-126); zero stays zero. */
+double oracle_round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  const double m = frexp(x, &e);           /* x = m 2^e, 0.5 <= |m| < 1 */
+  const double scaled = ldexp(m, 8);       /* 8 significant bits above the binary point */
+  double r = floor(scaled);
+  const double diff = scaled - r;
+  if (diff > 0.5 || (diff == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  return ldexp(r, e - 8);
+}
+
+void oracle_round_bf16_array(const double *x, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(x[i]);
+}
+
 /*
  * Causal depthwise conv1d + SiLU over a packed batch (the first part of the
  * GDN input prep).  x : [T, C];  w : [C, taps], tap taps-1 multiplies the
@@ -194,7 +216,8 @@ int oracle_conv_silu(int64_t T, int32_t N, int32_t C, int32_t taps, const double
  * Intermediates (q, k, v after prep; o) are fp64 throughout.
  */
 int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
-                     int32_t taps, double eps_l2, double eps_norm, const double *qkv,
+                     int32_t taps, double eps_l2, double eps_norm, int32_t bf16_points,
+                     const double *qkv,
                      const double *conv_w, const double *g, const double *beta,
                      const double *z, const double *norm_w, const int64_t *cu,
                      const double *h0, double *y, double *hT, int32_t nthreads) {
@@ -227,8 +250,17 @@ int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, i
     }
     memcpy(v + t * Cv, row + 2 * Cq, sizeof(double) * Cv);
   }
+  if (bf16_points) {
+    for (int64_t e = 0; e < T * Cq; ++e) {
+      q[e] = oracle_round_bf16(q[e]);
+      k[e] = oracle_round_bf16(k[e]);
+    }
+    for (int64_t e = 0; e < T * Cv; ++e) v[e] = oracle_round_bf16(v[e]);
+  }
   rc = oracle_gdn_fwd(T, N, Hk, Hv, dk, dv, q, k, v, g, beta, cu, h0, o, hT, nthreads);
   if (rc) goto done;
+  if (bf16_points)
+    for (int64_t e = 0; e < T * Cv; ++e) o[e] = oracle_round_bf16(o[e]);
   for (int64_t t = 0; t < T; ++t) {
     for (int32_t h = 0; h < Hv; ++h) {
       const double *os = o + (t * Hv + h) * dv;

@@ -304,17 +304,36 @@ def pin_mixer_torch(conv, mixer, fwd):
     z = rng.standard_normal((T, Hv, d))
     nw = 1 + 0.1 * rng.standard_normal(d)
     h0 = 0.1 * rng.standard_normal((2, Hv, d, d))
-    y, hT = mixer(qkv, cw, g, beta, z, nw, cu, h0, Hk=Hk, Hv=Hv, dk=d, dv=d)
     a = torch.from_numpy(_torch_conv_silu(qkv, cw, cu))
     # L2 norm x / sqrt(sum x^2 + 1e-6) through the library RMSNorm: rms_norm(x, eps/d) / sqrt(d)
     l2 = lambda x: F.rms_norm(x, (d,), eps=1e-6 / d) / np.sqrt(d)
-    q = l2(a[:, :Hk * d].reshape(T, Hk, d))
-    k = l2(a[:, Hk * d:2 * Hk * d].reshape(T, Hk, d))
-    v = a[:, 2 * Hk * d:].reshape(T, Hv, d)
-    o, hT2 = fwd(q.numpy(), k.numpy(), v.numpy(), g, beta, cu, h0)
-    y2 = F.rms_norm(torch.from_numpy(o), (d,), torch.from_numpy(nw), eps=1e-6) * F.silu(torch.from_numpy(z))
-    assert np.allclose(y, y2.numpy(), rtol=1e-11, atol=1e-12), "mixer y"
-    assert np.allclose(hT, hT2, rtol=1e-11, atol=1e-12), "mixer hT"
+    # bf16 rounding points through torch's own fp32 -> bf16 conversion (the prepped values are
+    # not ties at fp32 precision for these inputs, so fp64 -> fp32 -> bf16 is a single rounding)
+    to_bf16 = lambda x: x.float().to(torch.bfloat16).double()
+    for points in (False, True):
+        rnd = to_bf16 if points else (lambda x: x)
+        y, hT = mixer(qkv, cw, g, beta, z, nw, cu, h0, Hk=Hk, Hv=Hv, dk=d, dv=d, bf16_points=points)
+        q = rnd(l2(a[:, :Hk * d].reshape(T, Hk, d)))
+        k = rnd(l2(a[:, Hk * d:2 * Hk * d].reshape(T, Hk, d)))
+        v = rnd(a[:, 2 * Hk * d:].reshape(T, Hv, d))
+        o, hT2 = fwd(q.numpy(), k.numpy(), v.numpy(), g, beta, cu, h0)
+        o = rnd(torch.from_numpy(o))
+        y2 = F.rms_norm(o, (d,), torch.from_numpy(nw), eps=1e-6) * F.silu(torch.from_numpy(z))
+        assert np.allclose(y, y2.numpy(), rtol=1e-11, atol=1e-12), f"mixer y (bf16 points {points})"
+        assert np.allclose(hT, hT2, rtol=1e-11, atol=1e-12), f"mixer hT (bf16 points {points})"
 
 
-MIXER_PINS = [pin_conv_torch, pin_conv_delta_taps, pin_mixer_torch]
+def pin_round_bf16_matches_torch(conv, mixer, fwd, lib=None):
+    import torch
+    import oracle
+    rng = np.random.default_rng(34)
+    x = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-6, 6, 3000),
+                        np.array([1.0, -1.0, 0.0, 1.00390625, 1.01171875, 3.0e38, -2.5e-30])])
+    x32 = x.astype(np.float32).astype(np.float64)          # fp32-representable: one rounding in torch
+    ref = torch.from_numpy(x32).float().to(torch.bfloat16).double().numpy()
+    rnd = mixer.keywords["lib"] if hasattr(mixer, "keywords") and "lib" in mixer.keywords else None
+    got = oracle.round_bf16(x32, lib=rnd)
+    assert np.array_equal(got, ref), "bf16 rounding"
+
+
+MIXER_PINS = [pin_conv_torch, pin_conv_delta_taps, pin_mixer_torch, pin_round_bf16_matches_torch]

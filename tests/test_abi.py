@@ -1,0 +1,172 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every symbol include/gdn.h
+declares, and rejects every invalid argument with its status code before anything is enqueued.
+No call here reaches a kernel launch (all arguments are invalid by construction)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_chunked_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GDN_EXPORT\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_symbols() == sorted(gdn.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [s for s in declared_symbols() if s not in exported]
+    assert not missing, f"not exported: {missing}"
+    # nothing else with C linkage leaks out under the gdn_ prefix
+    extra = sorted(s for s in exported if s.startswith("gdn_") and s not in declared_symbols())
+    assert not extra, f"undeclared exports: {extra}"
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.gdn_abi_version() == 1
+    m = re.search(r"#define GDN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == gdn.gdn_abi_version()
+    names = ["GDN_OK", "GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_UNSUPPORTED", "GDN_ERR_ALIGN",
+             "GDN_ERR_WORKSPACE", "GDN_ERR_ALIAS", "GDN_ERR_HIP"]
+    for code, name in enumerate(names):
+        assert gdn.gdn_status_string(code).startswith(name)
+    assert "unknown" in gdn.gdn_status_string(99)
+    assert gdn.gdn_last_hip_error() == 0
+
+
+def test_workspace_size():
+    # slots = T // 64 + N; per slot: Hv records of 18944 B and Hk K^T records of 16384 B (256-aligned)
+    def expect(T, N, Hk, Hv):
+        r = lambda x: (x + 255) // 256 * 256
+        s = T // 64 + N
+        return r(s * Hv * 18944) + r(s * Hk * 16384)
+    for args in [(16384, 1, 16, 32), (677, 7, 16, 32), (0, 1, 4, 4), (1, 3, 1, 2)]:
+        assert gdn.gdn_chunk_fwd_workspace_size(*args) == expect(*args)
+    assert gdn.gdn_chunk_fwd_workspace_size(10, 1, 3, 4) == 0     # Hv % Hk != 0
+    assert gdn.gdn_chunk_fwd_workspace_size(10, 0, 1, 1) == 0     # N < 1
+    assert gdn.gdn_chunk_fwd_workspace_size(-1, 1, 1, 1) == 0     # T < 0
+    d = gdn.ChunkDesc(10, 1, 1, 1, 64, 128, None, 0)
+    assert gdn.lib().gdn_chunk_fwd_workspace_size(ctypes.byref(d)) == 0   # dk != 128
+    mix = gdn.gdn_mixer_fwd_workspace_size(936, 1, 16, 32)
+    assert mix > gdn.gdn_chunk_fwd_workspace_size(936, 1, 16, 32)
+    assert gdn.gdn_mixer_fwd_workspace_size(936, 1, 16, 32, conv_taps=3) == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# Validation: fake, well-separated device addresses; every call must fail before any launch.
+# ---------------------------------------------------------------------------------------------
+T, N, HK, HV = 100, 1, 2, 4
+GB = 1 << 30
+
+
+def _addrs():
+    # distinct 1 GiB-spaced, 256-aligned fake addresses (never dereferenced)
+    base = 0x7F0000000000
+    names = ["q", "k", "v", "g", "beta", "cu", "h0", "o", "hT", "ws"]
+    return {n: base + i * GB for i, n in enumerate(names)}
+
+
+def _call(desc=None, **over):
+    a = _addrs()
+    a.update(over)
+    ws_bytes = gdn.gdn_chunk_fwd_workspace_size(T, N, HK, HV)
+    d = desc if desc is not None else gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], ws_bytes)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return gdn.lib().gdn_chunk_fwd(ctypes.byref(d) if d is not False else None, P(a["q"]), P(a["k"]), P(a["v"]),
+                                   P(a["g"]), P(a["beta"]), P(a["cu"]), P(a["h0"]), P(a["o"]), P(a["hT"]), None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "beta", "cu", "o"])
+def test_null_pointers(field):
+    assert _call(**{field: None}) == gdn.GDN_ERR_NULL
+
+
+def test_null_descriptor():
+    assert _call(desc=False) == gdn.GDN_ERR_NULL
+
+
+def test_bad_shapes():
+    a = _addrs()
+    ws = gdn.gdn_chunk_fwd_workspace_size(T, N, HK, HV)
+    for bad in [gdn.ChunkDesc(T, 0, HK, HV, 128, 128, a["ws"], ws), gdn.ChunkDesc(-5, N, HK, HV, 128, 128, a["ws"], ws),
+                gdn.ChunkDesc(T, N, 3, HV, 128, 128, a["ws"], ws), gdn.ChunkDesc(T, N, 0, HV, 128, 128, a["ws"], ws)]:
+        assert _call(desc=bad) == gdn.GDN_ERR_SHAPE
+    for bad in [gdn.ChunkDesc(T, N, HK, HV, 64, 128, a["ws"], ws), gdn.ChunkDesc(T, N, HK, HV, 128, 256, a["ws"], ws)]:
+        assert _call(desc=bad) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    a = _addrs()
+    ws = gdn.gdn_chunk_fwd_workspace_size(T, N, HK, HV)
+    assert _call(desc=gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], ws - 1)) == gdn.GDN_ERR_WORKSPACE
+    assert _call(desc=gdn.ChunkDesc(T, N, HK, HV, 128, 128, None, ws)) == gdn.GDN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("field,off", [("q", 8), ("k", 2), ("v", 4), ("o", 8), ("h0", 4), ("hT", 12),
+                                       ("g", 2), ("beta", 1), ("cu", 2)])
+def test_alignment(field, off):
+    a = _addrs()
+    assert _call(**{field: a[field] + off}) == gdn.GDN_ERR_ALIGN
+
+
+def test_alignment_of_workspace():
+    a = _addrs()
+    ws = gdn.gdn_chunk_fwd_workspace_size(T, N, HK, HV)
+    assert _call(desc=gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"] + 8, ws)) == gdn.GDN_ERR_ALIGN
+
+
+def test_aliasing():
+    a = _addrs()
+    assert _call(o=a["q"]) == gdn.GDN_ERR_ALIAS                 # output over an input
+    assert _call(o=a["v"] + 1024) == gdn.GDN_ERR_ALIAS          # partial overlap
+    assert _call(hT=a["o"]) == gdn.GDN_ERR_ALIAS                # two outputs overlap
+    assert _call(hT=a["h0"] + 256) == gdn.GDN_ERR_ALIAS         # partial overlap with h0
+    assert _call(ws=a["k"]) == gdn.GDN_ERR_ALIAS                # workspace over an input
+
+
+def test_workspace_alias_with_input():
+    a = _addrs()
+    ws = gdn.gdn_chunk_fwd_workspace_size(T, N, HK, HV)
+    assert _call(desc=gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["k"], ws)) == gdn.GDN_ERR_ALIAS
+
+
+def test_mixer_validation():
+    a = _addrs()
+    ws = gdn.gdn_mixer_fwd_workspace_size(T, N, HK, HV)
+    P = ctypes.c_void_p
+
+    def call(m, **over):
+        b = {"qkv": a["q"], "cw": a["k"], "g": a["g"], "beta": a["beta"], "z": a["v"], "nw": a["h0"] + GB // 2,
+             "cu": a["cu"], "h0": a["h0"], "y": a["o"], "hT": a["hT"]}
+        b.update(over)
+        pp = lambda x: None if x is None else P(x)
+        return gdn.lib().gdn_mixer_fwd(ctypes.byref(m), pp(b["qkv"]), pp(b["cw"]), pp(b["g"]), pp(b["beta"]), pp(b["z"]),
+                                       pp(b["nw"]), pp(b["cu"]), pp(b["h0"]), pp(b["y"]), pp(b["hT"]), None)
+
+    good = lambda taps=4, eps=1e-6, wsb=ws: gdn.MixerDesc(gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], wsb), taps, eps)
+    assert call(good(taps=3)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(good(eps=0.0)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(good(wsb=ws - 1)) == gdn.GDN_ERR_WORKSPACE
+    assert call(good(), z=None) == gdn.GDN_ERR_NULL
+    assert call(good(), cw=a["k"] + 4) == gdn.GDN_ERR_ALIGN
+    assert call(good(), nw=a["h0"] + GB // 2 + 4) == gdn.GDN_ERR_ALIGN
+    assert call(good(), y=a["v"]) == gdn.GDN_ERR_ALIAS          # y over z
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdn, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        gdn.gdn_abi_version()

@@ -1,0 +1,89 @@
+"""gdn_mixer_fwd (HIP) against the fp64 mixer oracle: y rel-L2 <= 5e-3, an elementwise bound on y
+propagated from the 2e-2 max-abs tolerance of o through the gated RMSNorm (see check_mixer), and
+hT rel-L2 <= 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_chunked_amd as gdn
+import gdn_inputs as gi
+import oracle
+from tests.gpu_util import bf16_dev, f32_dev, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_mixer_gpu(m: gi.MixerInputs, Hk=16, Hv=32):
+    y, hT = gdn.gdn_mixer_fwd(bf16_dev(m.qkv), bf16_dev(m.conv_w), f32_dev(m.g), f32_dev(m.beta), bf16_dev(m.z),
+                              bf16_dev(m.norm_w), torch.from_numpy(m.cu.astype(np.int32)).cuda(),
+                              None if m.h0 is None else f32_dev(m.h0), Hk=Hk, Hv=Hv,
+                              cu_seqlens_host=torch.from_numpy(m.cu.astype(np.int64)))
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), hT.cpu().numpy().astype(np.float64)
+
+
+def run_mixer_oracle(m: gi.MixerInputs, Hk=16, Hv=32):
+    """(y, hT, o) from the fp64 oracle.  o, the rule's output at its bf16 rounding point, is not an
+    output of the mixer, so it is rebuilt from the oracle's pieces (conv + SiLU, L2 norm, bf16
+    rounding points, the rule); it only sets the scale of the elementwise bound on y."""
+    f = gi.bits_to_f64
+    h0 = None if m.h0 is None else m.h0.astype(np.float64)
+    y, hT = oracle.mixer_fwd(f(m.qkv), f(m.conv_w), m.g.astype(np.float64), m.beta.astype(np.float64), f(m.z),
+                             f(m.norm_w), m.cu.astype(np.int64), h0, Hk=Hk, Hv=Hv)
+    T, d = m.qkv.shape[0], 128
+    a = oracle.conv_silu(f(m.qkv), f(m.conv_w), m.cu.astype(np.int64))
+    l2 = lambda x: x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)
+    q = oracle.round_bf16(l2(a[:, :Hk * d].reshape(T, Hk, d)))
+    k = oracle.round_bf16(l2(a[:, Hk * d:2 * Hk * d].reshape(T, Hk, d)))
+    v = oracle.round_bf16(a[:, 2 * Hk * d:].reshape(T, Hv, d))
+    o, _ = oracle.gdn_fwd(q, k, v, m.g, m.beta, m.cu, h0)
+    return y, hT, oracle.round_bf16(o)
+
+
+def check_mixer(y, hT, y_ref, h_ref, o_ref, tag, m: gi.MixerInputs):
+    """Mixer tolerance, derived from the gdn_chunk_fwd tolerance on o.
+
+    y = o r c with r = 1 / rms(o_row) and c = w silu(z).  An absolute error e in o becomes
+    c r (e - o (o.e) / (d rms^2)) in y, at most |c| r |e|max (1 + |o| / rms); the bf16 output adds
+    at most half an ulp (2^-9 |y|).  So elementwise |dy| <= |c| r 2e-2 (1 + |o| r) + 2^-8 |y_ref|,
+    with 2e-2 the max-abs tolerance of o.  Also y rel-L2 <= 5e-3 and hT rel-L2 <= 1e-3."""
+    ry = rel_l2(y, y_ref)
+    rh = rel_l2(hT, h_ref)
+    zf = gi.bits_to_f64(m.z)
+    c = np.abs(gi.bits_to_f64(m.norm_w) * zf / (1 + np.exp(-zf)))
+    r = 1.0 / np.sqrt(np.mean(o_ref ** 2, axis=-1, keepdims=True) + 1e-6)
+    bound = c * r * 2e-2 * (1 + np.abs(o_ref) * r) + 2.0 ** -8 * np.abs(y_ref)
+    ratio = np.abs(y - y_ref) / bound
+    i = np.unravel_index(np.argmax(ratio), ratio.shape) if ratio.size else None
+    worst = float(ratio[i]) if i is not None else 0.0
+    detail = "" if i is None else (f" at {i}: |dy| {abs(y[i] - y_ref[i]):.3e} y {y_ref[i]:.3e} "
+                                   f"rms(o_row) {1 / r[i[0], i[1], 0]:.3e}")
+    say(f"  {tag}: y rel-L2 {ry:.3e} max |dy|/bound {worst:.3f}{detail} | hT rel-L2 {rh:.3e}")
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hT))
+    assert ry <= 5e-3 and worst <= 1.0 and rh <= 1e-3
+
+
+def test_mixer_t936_layer0():
+    say("[mixer] T=936 Hk=16 Hv=32 seed=100")
+    m = gi.make_mixer_inputs(100)
+    check_mixer(*run_mixer_gpu(m), *run_mixer_oracle(m), "T=936", m)
+
+
+def test_mixer_varlen_conv_resets_with_h0():
+    lengths = [5, 70, 3, 130, 1]
+    say(f"[mixer] varlen {lengths} Hk=2 Hv=4 with h0")
+    m = gi.make_mixer_inputs(7, lengths=lengths, Hk=2, Hv=4, with_h0=True)
+    check_mixer(*run_mixer_gpu(m, 2, 4), *run_mixer_oracle(m, 2, 4), "varlen", m)
+
+
+def test_mixer_varlen_bitwise_equals_separate():
+    lengths = [40, 3, 90]
+    say(f"[mixer] varlen bitwise {lengths}")
+    m = gi.make_mixer_inputs(8, lengths=lengths, Hk=2, Hv=4, with_h0=True)
+    y, hT = run_mixer_gpu(m, 2, 4)
+    for n, L in enumerate(lengths):
+        sl = slice(m.cu[n], m.cu[n + 1])
+        ms = gi.MixerInputs(m.qkv[sl], m.conv_w, m.beta[sl], m.g[sl], m.z[sl], m.norm_w,
+                            np.array([0, L], np.int32), m.h0[n:n + 1])
+        y1, h1 = run_mixer_gpu(ms, 2, 4)
+        assert np.array_equal(y[sl], y1) and np.array_equal(hT[n], h1[0])

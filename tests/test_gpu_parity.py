@@ -1,0 +1,161 @@
+"""gdn_chunk_fwd (HIP, through the C ABI) against the fp64 oracle on the same seeded inputs,
+element by element: o rel-L2 <= 5e-3 and max-abs <= 2e-2, hT rel-L2 <= 1e-3.  Plus bitwise
+invariants of the implementation (varlen packing, determinism, dirty workspace, continuation)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_chunked_amd as gdn
+import gdn_inputs as gi
+from tests.gpu_util import check, dev_inputs, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", list(gi.CASES))
+def test_parity_workloads(name):
+    c = gi.CASES[name]
+    say(f"[parity] {name}: T={c.T} N={c.N} Hk={c.Hk} Hv={c.Hv} seed={c.seed} h0={c.with_h0}")
+    x = gi.make_case(name)
+    o, hT = run_gpu(x)
+    o_ref, h_ref = run_oracle(x)
+    check(o, hT, o_ref, h_ref, name)
+
+
+def test_ragged_lengths_batch():
+    lengths = [1, 2, 63, 64, 65, 127, 128, 129, 191, 192, 193]
+    say(f"[ragged] lengths={lengths} Hk=2 Hv=4")
+    x = gi.make_gdn_inputs(2, 4, lengths, seed=40, with_h0=True)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), "ragged batch")
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 127, 128, 129, 191, 192, 193])
+def test_single_lengths(L):
+    say(f"[single] L={L} Hk=1 Hv=2")
+    x = gi.make_gdn_inputs(1, 2, [L], seed=41 + L, with_h0=(L % 2 == 1))
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), f"L={L}")
+
+
+def test_varlen_bitwise_equals_separate_runs():
+    lengths = [61, 0, 130, 64, 1, 200]
+    say(f"[varlen-bitwise] lengths={lengths}")
+    x = gi.make_gdn_inputs(2, 4, lengths, seed=50, with_h0=True)
+    o, hT = run_gpu(x)
+    cu = x.cu
+    for n, L in enumerate(lengths):
+        sl = slice(cu[n], cu[n + 1])
+        xs = gi.GdnInputs(x.q[sl], x.k[sl], x.v[sl], x.beta[sl], x.g[sl], np.array([0, L], np.int32), x.h0[n:n + 1])
+        o1, h1 = run_gpu(xs)
+        assert np.array_equal(o[sl], o1), f"sequence {n}: output differs"
+        assert np.array_equal(hT[n], h1[0]), f"sequence {n}: state differs"
+
+
+def test_determinism_and_dirty_workspace():
+    say("[determinism] t539_h16x32 x3 with poisoned workspace/outputs")
+    x = gi.make_case("t539_h16x32")
+    d = dev_inputs(x)
+    T, N = int(x.cu[-1]), len(x.cu) - 1
+    ws_n = gdn.gdn_chunk_fwd_workspace_size(T, N, 16, 32)
+    outs = []
+    for fill in (0x00, 0xFF, 0x7F):
+        ws = torch.full((ws_n,), fill, dtype=torch.uint8, device="cuda")
+        o = torch.full((T, 32, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        hT = torch.full((N, 32, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], None, o=o, hT=hT, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy(), hT.cpu().numpy()))
+    for o_, h_ in outs[1:]:
+        assert np.array_equal(o_, outs[0][0]) and np.array_equal(h_, outs[0][1])
+
+
+def test_changed_input_replay():
+    say("[replay] same shape, inputs A, B, A")
+    xa = gi.make_gdn_inputs(4, 8, [300], seed=60)
+    xb = gi.make_gdn_inputs(4, 8, [300], seed=61)
+    ra1, rb, ra2 = run_gpu(xa), run_gpu(xb), run_gpu(xa)
+    assert np.array_equal(ra1[0], ra2[0]) and np.array_equal(ra1[1], ra2[1])
+    assert not np.array_equal(ra1[0], rb[0])
+    check(rb[0], rb[1], *run_oracle(xb), "B")
+
+
+def test_h0_none_hT_none_and_in_place():
+    say("[state-args] h0=None vs zeros, hT=None, hT aliasing h0")
+    x = gi.make_gdn_inputs(2, 4, [100, 37], seed=70)
+    d = dev_inputs(x)
+    cu_h = torch.from_numpy(x.cu.astype(np.int64))
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"])
+    o1, h1 = gdn.gdn_chunk_fwd(*args, None, cu_seqlens_host=cu_h)
+    z = torch.zeros((2, 4, 128, 128), dtype=torch.float32, device="cuda")
+    o2, h2 = gdn.gdn_chunk_fwd(*args, z, cu_seqlens_host=cu_h)
+    o3, h3 = gdn.gdn_chunk_fwd(*args, None, want_state=False, cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    assert h3 is None
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(h1, h2)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    # in-place continuation: hT is h0
+    h0 = torch.from_numpy((0.05 * np.random.default_rng(1).standard_normal((2, 4, 128, 128))).astype(np.float32)).cuda()
+    o4, h4 = gdn.gdn_chunk_fwd(*args, h0.clone(), cu_seqlens_host=cu_h)
+    buf = h0.clone()
+    o5, h5 = gdn.gdn_chunk_fwd(*args, buf, hT=buf, cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    assert h5.data_ptr() == buf.data_ptr()
+    assert torch.equal(o4.view(torch.int16), o5.view(torch.int16)) and torch.equal(h4, buf)
+
+
+@pytest.mark.parametrize("split", [128, 100])
+def test_continuation(split):
+    say(f"[continuation] T=300 split={split}")
+    x = gi.make_gdn_inputs(2, 4, [300], seed=80, with_h0=True)
+    o, hT = run_gpu(x)
+    a = gi.GdnInputs(x.q[:split], x.k[:split], x.v[:split], x.beta[:split], x.g[:split],
+                     np.array([0, split], np.int32), x.h0)
+    oa, ha = run_gpu(a)
+    b = gi.GdnInputs(x.q[split:], x.k[split:], x.v[split:], x.beta[split:], x.g[split:],
+                     np.array([0, 300 - split], np.int32), ha.astype(np.float32))
+    ob, hb = run_gpu(b)
+    oc = np.concatenate([oa, ob])
+    if split % 64 == 0:
+        assert np.array_equal(oc, o) and np.array_equal(hb, hT), "split at a chunk boundary must be bitwise"
+    check(oc, hb, *run_oracle(x), f"split {split}")
+
+
+def test_h0_sensitivity_slow_decay():
+    say("[h0-sensitivity] g = log sigmoid(N(6,1)), non-symmetric h0")
+    x = gi.make_gdn_inputs(2, 4, [150, 70], seed=90, with_h0=True, h0_std=0.5, g_mean=6.0)
+    assert not np.allclose(x.h0[0, 0], x.h0[0, 0].T)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), "slow decay")
+
+
+@pytest.mark.parametrize("Hk,Hv", [(4, 4), (2, 4), (1, 4), (16, 32)])
+def test_head_ratios(Hk, Hv):
+    say(f"[gqa] Hk={Hk} Hv={Hv}")
+    x = gi.make_gdn_inputs(Hk, Hv, [97, 160], seed=100 + Hk * 10 + Hv, with_h0=True)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), f"Hk={Hk} Hv={Hv}")
+
+
+def test_extreme_gates():
+    say("[extreme] g=-30 spikes, beta in {0, 1}")
+    x = gi.make_gdn_inputs(2, 4, [200], seed=110, with_h0=True)
+    rng = np.random.default_rng(111)
+    x.g[rng.random(x.g.shape) < 0.05] = -30.0
+    x.beta[rng.random(x.beta.shape) < 0.1] = 0.0
+    x.beta[rng.random(x.beta.shape) < 0.1] = 1.0
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), "extreme gates")
+
+
+def test_empty_batch_keeps_state():
+    say("[empty] T=0, N=3")
+    h0 = (0.1 * np.random.default_rng(3).standard_normal((3, 4, 128, 128))).astype(np.float32)
+    x = gi.GdnInputs(np.zeros((0, 2, 128), np.uint16), np.zeros((0, 2, 128), np.uint16),
+                     np.zeros((0, 4, 128), np.uint16), np.zeros((0, 4), np.float32), np.zeros((0, 4), np.float32),
+                     np.zeros(4, np.int32), h0)
+    o, hT = run_gpu(x)
+    assert o.shape == (0, 4, 128) and np.array_equal(hT, h0.astype(np.float64))
+    x.h0 = None
+    o, hT = run_gpu(x)
+    assert np.all(hT == 0)

@@ -53,6 +53,9 @@ MUTANTS = {
     "rmsnorm_sum_not_mean": [("sqrt(ms / dv + eps_norm)", "sqrt(ms + eps_norm)")],
     "gate_without_silu": [("norm_w[j] * zs[j] * sigmoid(zs[j])", "norm_w[j] * sigmoid(zs[j])")],
     "l2norm_missing_on_k": [("k[(t * Hk + hh) * dk + j] = ks[j] * rk;", "k[(t * Hk + hh) * dk + j] = ks[j];")],
+    "bf16_ties_away": [("(diff == 0.5 && fmod(r, 2.0) != 0.0)", "(diff == 0.5)")],
+    "bf16_truncates": [("if (diff > 0.5 ||", "if (0 &&")],
+    "bf16_point_on_o_missing": [("for (int64_t e = 0; e < T * Cv; ++e) o[e] = oracle_round_bf16(o[e]);", ";")],
 }
 
 
