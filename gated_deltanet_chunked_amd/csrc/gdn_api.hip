@@ -10,8 +10,8 @@
 
 namespace gdn {
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
-                       const int32_t *cu, int N, int Hk, int Hv, int64_t nslots, void *rec,
-                       void *kcrec, hipStream_t stream);
+                       const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
+                       void *rec, void *kcrec, hipStream_t stream);
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, void *o, float *hT, const void *rec, const void *kcrec,
                        int N, int Hk, int Hv, hipStream_t stream);
@@ -55,7 +55,7 @@ int check_shape(const gdn_chunk_desc *d, Shape &s) {
   if (d->num_seqs < 1 || d->total_tokens < 0 || d->num_k_heads < 1 || d->num_v_heads < 1)
     return GDN_ERR_SHAPE;
   if (d->num_v_heads % d->num_k_heads != 0) return GDN_ERR_SHAPE;
-  if (d->total_tokens > INT32_MAX - 2 * gdn::kChunk || d->num_k_heads > 65535) return GDN_ERR_SHAPE;
+  if (d->total_tokens > INT32_MAX - 2 * gdn::kChunk || d->num_v_heads > 65535) return GDN_ERR_SHAPE;
   const int64_t blocks = (int64_t)d->num_seqs * d->num_v_heads * gdn::kDvTiles;
   if (blocks > INT32_MAX) return GDN_ERR_SHAPE;
   s.T = d->total_tokens;
@@ -123,7 +123,7 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
   unsigned char *kcrec = rec + s.rec_bytes;
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   if ((stage & kPrep) && s.T > 0) {
-    gdn::launch_chunk_prep(q, k, g, beta, cu, s.N, s.Hk, s.Hv, s.nslots, rec, kcrec, stream);
+    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec, kcrec, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
   }

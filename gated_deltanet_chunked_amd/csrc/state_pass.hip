@@ -19,6 +19,8 @@
 //
 // Operands reach registers straight from global memory (one chunk ahead, double-buffered in
 // registers); LDS only carries the three cross-wave exchanges per chunk: bf16 H, R and U~.
+// A fifth wave hides HBM latency: it runs kTouchAhead chunks ahead and pulls every line the
+// compute waves will load into L2, so their one-chunk-ahead register prefetch hits in L2.
 #include "gdn_device.h"
 
 namespace gdn {
@@ -27,6 +29,48 @@ namespace {
 
 constexpr int kPitchH = kDim + 8;     // Ht row pitch (bf16): value column j, key index
 constexpr int kPitchT = kChunk + 8;   // Rh/Rl/Uh/Ul/Uo row pitch (bf16): value column j, token
+constexpr int kComputeWaves = 4;
+constexpr int kThreads = 64 * (kComputeWaves + 1);  // + one L2-warming wave
+constexpr int kTouchAhead = 4;        // chunks the warming wave runs ahead of the compute waves
+
+// One 4-byte load per lane, delivered straight into a scratch LDS word (global_load_lds_dword):
+// it pulls the 128-byte line into L2 without occupying a VGPR, so the warming wave never has to
+// wait for it.  Lane i writes LDS byte lds_dummy + 4 i.
+__device__ __forceinline__ void touch(const void *p, unsigned lds_dummy) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_dummy), "v"(p)
+               : "memory");
+}
+
+// Bring chunk c's operands into L2: the lead workgroup of each sharing group touches the data it
+// shares (K, Q and K^T of the k-head; the v-head's record), every workgroup touches its V slice.
+__device__ __forceinline__ void touch_chunk(int c, int tb, int te, int slot0, int hk, int h, int Hk,
+                                            int Hv, int d0, bool lead_k, bool lead_v, int l,
+                                            const unsigned short *q, const unsigned short *k,
+                                            const unsigned short *v, const uint8_t *rec,
+                                            const uint8_t *kcrec, unsigned lds_dummy) {
+  const int t0 = tb + kChunk * c;
+  const int L = min(kChunk, te - t0);
+  const int row = min(l, L - 1);
+  const size_t slot = (size_t)slot0 + c;
+  if (lead_k) {
+    const unsigned short *kr = k + ((size_t)(t0 + row) * Hk + hk) * kDim;
+    const unsigned short *qr = q + ((size_t)(t0 + row) * Hk + hk) * kDim;
+    touch(kr, lds_dummy);
+    touch(kr + 64, lds_dummy);
+    touch(qr, lds_dummy);
+    touch(qr + 64, lds_dummy);
+    const uint8_t *kc = kcrec + (slot * Hk + hk) * kKcBytes + l * 128;
+    touch(kc, lds_dummy);
+    touch(kc + 8192, lds_dummy);
+  }
+  if (lead_v) {
+    const uint8_t *rp = rec + (slot * Hv + h) * kRecBytes;
+    touch(rp + l * 128, lds_dummy);
+    touch(rp + 8192 + l * 128, lds_dummy);
+    touch(rp + 16384 + min(l, (kRecBytes - 16384) / 128 - 1) * 128, lds_dummy);
+  }
+  touch(v + ((size_t)(t0 + row) * Hv + h) * kDim + d0, lds_dummy);
+}
 
 // Operands of one chunk, exactly as loaded: nothing here is touched until the chunk is
 // processed, so the loads stay in flight while the previous chunk computes.
@@ -202,7 +246,7 @@ __device__ __forceinline__ void chunk_step(const ChunkOps &cur, int t0, int te, 
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void state_pass_kernel(
+__global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const float *h0, unsigned short *__restrict__ o, float *hT,  // hT may equal h0
@@ -213,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void state_pass_kernel(
   __shared__ __attribute__((aligned(16))) unsigned short Uh[kDvTile * kPitchT];
   __shared__ __attribute__((aligned(16))) unsigned short Ul[kDvTile * kPitchT];
   __shared__ __attribute__((aligned(16))) unsigned short Uo[kDvTile * kPitchT];
+  __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
 
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tile = lid % kDvTiles;
@@ -225,6 +270,28 @@ __global__ __launch_bounds__(256, 1) void state_pass_kernel(
   const int nc = (te - tb + kChunk - 1) / kChunk;
   const int slot0 = tb / kChunk + n;
   const size_t state_base = ((size_t)n * Hv + h) * kDim * kDim;
+
+  if (w == kComputeWaves) {
+    // L2-warming wave: stays kTouchAhead chunks ahead, joining the compute waves' barriers (one
+    // before the loop, three per chunk) so it neither lags nor runs away.
+    const unsigned sink = (unsigned)(uintptr_t)touch_sink;
+    const bool lead_v = tile == 0, lead_k = lead_v && (h % (Hv / Hk)) == 0;
+    if (nc > 0) {
+      for (int c = 0; c < min(kTouchAhead, nc); ++c)
+        touch_chunk(c, tb, te, slot0, hk, h, Hk, Hv, d0, lead_k, lead_v, l, q, k, v, rec, kcrec, sink);
+      __syncthreads();
+      for (int c = 0; c < nc; ++c) {
+        if (c + kTouchAhead < nc)
+          touch_chunk(c + kTouchAhead, tb, te, slot0, hk, h, Hk, Hv, d0, lead_k, lead_v, l, q, k, v, rec,
+                      kcrec, sink);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the workgroup ends
+    return;
+  }
 
   // State slice: H[a][rr] = H[key 32w + 16a + 4 lg + rr][value d0 + lj].
   f32x4 H[2];
@@ -274,7 +341,7 @@ void launch_state_pass(const void *q, const void *k, const void *v, const int32_
                        const float *h0, void *o, float *hT, const void *rec, const void *kcrec,
                        int N, int Hk, int Hv, hipStream_t stream) {
   const unsigned nblocks = (unsigned)N * (unsigned)Hv * kDvTiles;
-  hipLaunchKernelGGL(state_pass_kernel, dim3(nblocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(state_pass_kernel, dim3(nblocks), dim3(kThreads), 0, stream,
                      static_cast<const unsigned short *>(q), static_cast<const unsigned short *>(k),
                      static_cast<const unsigned short *>(v), cu, h0,
                      static_cast<unsigned short *>(o), hT, static_cast<const uint8_t *>(rec),
