@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
-REC_BYTES, KC_BYTES = 18944, 16384   # per-(chunk, v-head) and per-(chunk, k-head) workspace records
+REC_BYTES = 18944             # per-(chunk, v-head) workspace record
 D = 128
 
 
@@ -56,12 +56,12 @@ def path_flops(T, Hk, Hv):
 
 
 def prep_bytes(T, Hk, Hv, nch):
-    return T * Hk * D * 2 * 2 + T * Hv * 8 + nch * (Hv * REC_BYTES + Hk * KC_BYTES)
+    return T * Hk * D * 2 * 2 + T * Hv * 8 + nch * Hv * REC_BYTES
 
 
 def pass_bytes(T, N, Hk, Hv, nch, with_h0):
     state = N * Hv * D * D * 4
-    return (T * Hk * D * 2 * 2 + T * Hv * D * 2 + nch * (Hv * REC_BYTES + Hk * KC_BYTES)
+    return (T * Hk * D * 2 * 2 + T * Hv * D * 2 + nch * Hv * REC_BYTES
             + T * Hv * D * 2 + state * (2 if with_h0 else 1))
 
 

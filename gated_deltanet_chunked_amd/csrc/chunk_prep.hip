@@ -16,8 +16,7 @@
 //      lane), then the off-diagonal blocks by T_ij = -T_ii sum_m A_im T_mj on fp32 MFMA, one
 //      sub-diagonal at a time.
 //   4. T' = T diag(beta) as bf16 hi + lo MFMA fragments, P as bf16 fragments, e^{G} and
-//      e^{G_last - G} -> the record the state pass reads.  The first v-head of each k-head group
-//      also writes K^T as MFMA fragments.
+//      e^{G_last - G} -> the record the state pass reads.
 // Every exponent is <= 0 (G is non-increasing), so no e^{-G} is ever formed.  Tokens past the
 // end of a sequence enter as k = q = 0, g = 0, beta = 0, which leaves T' and P zero on them.
 #include "gdn_device.h"
@@ -68,8 +67,7 @@ __device__ __forceinline__ int find_sequence(const int32_t *__restrict__ cu, int
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec,
-    uint8_t *__restrict__ kcrec) {
+    const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   unsigned char *Ks = smem + kOffKs;
   unsigned char *Qs = smem + kOffQs;
@@ -142,23 +140,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
       const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Am + swz(16 * rb + lj, ch * 8));
       const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(Ks + swz(16 * cb + lj, ch * 8));
       acc[it] = mfma_bf16(a, bb, acc[it]);
-    }
-  }
-  // K^T fragments for the state pass (first v-head of the group): fragment (rb, ks), lane ll
-  // holds K[token 32 ks + 8 (ll/16) + e][dk 16 rb + ll % 16], e = 0..7.
-  if (h % r == 0) {
-    uint8_t *kcp = kcrec + ((size_t)slot * Hk + hk) * kKcBytes;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int s = tid + 256 * it, f = s >> 6, ll = s & 63;
-      const int rb = f >> 1, ks = f & 1;
-      const int dk = 16 * rb + (ll & 15);
-      const int tok0 = 32 * ks + 8 * (ll >> 4);
-      u16x8 vals;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vals[e] = *reinterpret_cast<const unsigned short *>(Ks + swz(tok0 + e, dk));
-      *reinterpret_cast<u16x8 *>(kcp + f * kFragBytes + ll * 16) = vals;
     }
   }
   __syncthreads();  // Ks, Qs are dead from here on; As, Ps take their space
@@ -274,12 +255,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, void *kcrec, hipStream_t stream) {
+                       void *rec, hipStream_t stream) {
   dim3 grid((unsigned)nslots, (unsigned)Hv);
   hipLaunchKernelGGL(chunk_prep_kernel, grid, dim3(256), 0, stream,
                      static_cast<const unsigned short *>(q), static_cast<const unsigned short *>(k),
-                     g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec),
-                     static_cast<uint8_t *>(kcrec));
+                     g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec));
 }
 
 }  // namespace gdn

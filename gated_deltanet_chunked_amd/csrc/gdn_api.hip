@@ -11,10 +11,10 @@
 namespace gdn {
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, void *kcrec, hipStream_t stream);
+                       void *rec, hipStream_t stream);
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
-                       const float *h0, void *o, float *hT, const void *rec, const void *kcrec,
-                       int N, int Hk, int Hv, hipStream_t stream);
+                       const float *h0, void *o, float *hT, const void *rec, int N, int Hk, int Hv,
+                       hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, void *q, void *k, void *v, hipStream_t stream);
 void launch_gated_rmsnorm(const void *o, const void *z, const void *norm_w, float eps, int64_t T,
@@ -46,7 +46,7 @@ struct Shape {
   int64_t T;
   int N, Hk, Hv;
   int64_t nslots;
-  size_t rec_bytes, kc_bytes;  // workspace sections of the chunk path
+  size_t rec_bytes;  // workspace of the chunk path: one record per (chunk slot, v-head)
 };
 
 int check_shape(const gdn_chunk_desc *d, Shape &s) {
@@ -65,7 +65,6 @@ int check_shape(const gdn_chunk_desc *d, Shape &s) {
   s.nslots = gdn::num_slots(s.T, s.N);
   if (s.nslots > INT32_MAX) return GDN_ERR_SHAPE;
   s.rec_bytes = round_up((size_t)s.nslots * s.Hv * gdn::kRecBytes);
-  s.kc_bytes = round_up((size_t)s.nslots * s.Hk * gdn::kKcBytes);
   return GDN_OK;
 }
 
@@ -89,7 +88,7 @@ int check_chunk_args(const gdn_chunk_desc *d, Shape &s, Stage stage, const void 
   if (tok && (!q || !k)) return GDN_ERR_NULL;
   if (tok && prep && (!g || !beta)) return GDN_ERR_NULL;
   if (tok && pass && (!v || !o)) return GDN_ERR_NULL;
-  const size_t need = s.rec_bytes + s.kc_bytes;
+  const size_t need = s.rec_bytes;
   if (!d->workspace || d->workspace_bytes < need) return GDN_ERR_WORKSPACE;
   if (!prep) g = beta = nullptr;
   if (!pass) v = nullptr, h0 = nullptr, o = nullptr, hT = nullptr;
@@ -120,15 +119,14 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
               const float *g, const float *beta, const int32_t *cu, const float *h0, void *o,
               float *hT, void *ws, hipStream_t stream) {
   unsigned char *rec = static_cast<unsigned char *>(ws);
-  unsigned char *kcrec = rec + s.rec_bytes;
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   if ((stage & kPrep) && s.T > 0) {
-    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec, kcrec, stream);
+    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
   }
   if (stage & kPass) {
-    gdn::launch_state_pass(q, k, v, cu, h0, o, hT, rec, kcrec, s.N, s.Hk, s.Hv, stream);
+    gdn::launch_state_pass(q, k, v, cu, h0, o, hT, rec, s.N, s.Hk, s.Hv, stream);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;
@@ -159,7 +157,7 @@ int gdn_last_hip_error(void) { return g_last_hip_error; }
 size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d) {
   Shape s;
   if (check_shape(d, s) != GDN_OK) return 0;
-  return s.rec_bytes + s.kc_bytes;
+  return s.rec_bytes;
 }
 
 int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
@@ -208,7 +206,7 @@ int mixer_layout(const gdn_mixer_desc *d, MixerLayout &m) {
   if (d->conv_taps != 4) return GDN_ERR_UNSUPPORTED;
   if (!(d->norm_eps > 0.f)) return GDN_ERR_UNSUPPORTED;
   if ((int64_t)(2 * m.s.Hk + m.s.Hv) * gdn::kDim > INT32_MAX / 2) return GDN_ERR_SHAPE;
-  m.chunk_bytes = m.s.rec_bytes + m.s.kc_bytes;
+  m.chunk_bytes = m.s.rec_bytes;
   m.q_bytes = round_up((size_t)m.s.T * m.s.Hk * gdn::kDim * 2);
   m.v_bytes = round_up((size_t)m.s.T * m.s.Hv * gdn::kDim * 2);
   m.total = m.chunk_bytes + 2 * m.q_bytes + 2 * m.v_bytes;

@@ -38,9 +38,6 @@ constexpr int kRecP = kRecTpLo + kFrags * kFragBytes;     // P = tril(Q K^T o e^
 constexpr int kRecEG = kRecP + kFrags * kFragBytes;       // e^{G_i}           fp32[64]
 constexpr int kRecED = kRecEG + kChunk * 4;               // e^{G_last - G_i}  fp32[64]
 constexpr int kRecBytes = kRecED + kChunk * 4;            // 18944
-// ---- per-(chunk slot, k-head) record: K^T as 16 A-operand fragments (dk block rb, token step ks)
-constexpr int kKcFrags = 16;                              // fragment rb * 2 + ks
-constexpr int kKcBytes = kKcFrags * kFragBytes;           // 16384
 
 __host__ __device__ constexpr int frag_row_block(int f) { return f < 2 ? f : (f < 4 ? 2 : 3); }
 __host__ __device__ constexpr int frag_k_step(int f) { return (f == 3 || f == 5) ? 1 : 0; }

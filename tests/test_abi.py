@@ -47,11 +47,11 @@ def test_abi_version_and_status_strings():
 
 
 def test_workspace_size():
-    # slots = T // 64 + N; per slot: Hv records of 18944 B and Hk K^T records of 16384 B (256-aligned)
+    # slots = T // 64 + N; per slot: Hv records of 18944 B (256-aligned)
     def expect(T, N, Hk, Hv):
         r = lambda x: (x + 255) // 256 * 256
         s = T // 64 + N
-        return r(s * Hv * 18944) + r(s * Hk * 16384)
+        return r(s * Hv * 18944)
     for args in [(16384, 1, 16, 32), (677, 7, 16, 32), (0, 1, 4, 4), (1, 3, 1, 2)]:
         assert gdn.gdn_chunk_fwd_workspace_size(*args) == expect(*args)
     assert gdn.gdn_chunk_fwd_workspace_size(10, 1, 3, 4) == 0     # Hv % Hk != 0
