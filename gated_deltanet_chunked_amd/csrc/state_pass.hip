@@ -22,8 +22,8 @@
 //     (T' hi/lo, P, decays) and the V tile into a 3-deep LDS ring with global->LDS loads
 //     (global_load_lds_dwordx4: 1 KiB contiguous per instruction, no VGPRs), two chunks ahead of
 //     the compute waves, and pulls the Q rows of the chunk after that into L2.
-//   * The compute waves read every operand from LDS (K^T fragments are gathered from the same
-//     K tile), except Q, which they load into registers one chunk ahead.
+//   * The compute waves read every operand from LDS (K^T fragments come from the same K tile
+//     through transposing LDS reads), except Q, which they load into registers one chunk ahead.
 //   * LDS also carries the three cross-wave exchanges per chunk: bf16 H, R and U~.
 #include "gdn_device.h"
 
@@ -86,6 +86,12 @@ __device__ __forceinline__ void store_u32x2(unsigned short *dst, uint32_t a, uin
 __device__ __forceinline__ bf16x8 lds_bf16x8(const void *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+// Transposing LDS read of 4 bf16 per lane (gfx950 ds_read_b64_tr_b16); p is 8-byte aligned LDS.
+__device__ __forceinline__ v4i16 lds_read_tr16(const void *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+}
 
 // Producer: one chunk's K tile, record and V tile into a ring stage (kDmaPerChunk instructions,
 // issued unconditionally so the vmcnt bookkeeping is static; rows past the sequence end are
@@ -146,19 +152,22 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
   const int L = min(kChunk, te - t0);
   const unsigned char *rs = st + kStRec;
 
-  // K^T fragments for the state update, gathered from the K tile: fragment (key block 2w + a,
-  // token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][key 32 w + 16 a + lj].
+  // K^T fragments for the state update, read transposed from the K tile: fragment (key block
+  // 2w + a, token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][key 32 w + 16 a + lj].
+  // ds_read_b64_tr_b16: within each 16-lane group, lane r names 4 consecutive bf16 (row r of a
+  // 16 x 4 matrix M) and lane i receives M[4 j + i / 4][i % 4], j = 0..3.  With lane r = 4 j + q
+  // naming K[token t + j][key base + 4 q .. + 3], lane i receives K[t .. t + 3][base + i]: half a
+  // fragment (4 tokens) per read.
   bf16x8 kc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u16x8 vals;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vals[e] = *reinterpret_cast<const unsigned short *>(
-            st + kStK + swz(32 * ks + 8 * lg + e, 32 * w + 16 * a + lj));
-      kc[a][ks] = __builtin_bit_cast(bf16x8, vals);
+      const int key = 32 * w + 16 * a + 4 * (lj & 3);
+      const int tok = 32 * ks + 8 * lg + (lj >> 2);
+      const v4i16 lo4 = lds_read_tr16(st + kStK + swz(tok, key));
+      const v4i16 hi4 = lds_read_tr16(st + kStK + swz(tok + 4, key));
+      kc[a][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
   // X = K H and Q H (contraction over the 128 keys; B operand = bf16 H from LDS)
