@@ -3,7 +3,7 @@
 // The "open-jev-fast" README ("Phase 3", item 1) keeps the fp32 recurrent state in registers and
 // passes only the state from chunk to chunk.  Here one workgroup owns one (sequence, v-head,
 // 16-column slice of the 128 value columns): the state slice H[:, cols] (128 x 16 fp32) lives in
-// MFMA accumulators, spread over 4 compute waves (wave w holds key rows 32w .. 32w+31), and the
+// MFMA accumulators, spread over 4 compute waves (32 key rows each, see state_key), and the
 // chunks of the sequence are walked in order.  Sequences, heads and slices run in parallel.
 //
 // With H = S^T (key-major), local cumsum G, T' = (I + A)^-1 diag(beta) and
@@ -17,36 +17,51 @@
 // The hi/lo splits keep the state path at about 16 significant bits per operand, so the fp32
 // state does not drift over hundreds of chunks; bf16 is used where only the output sees it.
 //
-// Data movement (one producer wave + four compute waves per workgroup):
-//   * The producer wave streams each chunk's K tile (XOR-swizzled rows), the v-head's record
-//     (T' hi/lo, P, decays) and the V tile into a 3-deep LDS ring with global->LDS loads
-//     (global_load_lds_dwordx4: 1 KiB contiguous per instruction, no VGPRs), two chunks ahead of
-//     the compute waves, and pulls the Q rows of the chunk after that into L2.
-//   * The compute waves read every operand from LDS (K^T fragments come from the same K tile
-//     through transposing LDS reads), except Q, which they load into registers one chunk ahead.
-//   * LDS also carries the three cross-wave exchanges per chunk: bf16 H, R and U~.
+// A chunk takes three phases on the compute waves, separated by workgroup barriers b1, b2, b3:
+//   phase 1: K^T fragments, X and Q H from the K/Q/V tiles; R to LDS            -> b1
+//   phase 2: U~ = T' R; U~ (decayed hi/lo and plain) to LDS                      -> b2
+//   phase 3: o = e^G o (Q H) + P U~ to an LDS staging slot; H update; bf16 H     -> b3
+// Data movement (four producer waves + four compute waves per workgroup, one of each per SIMD):
+//   * The producer waves do all of the global memory traffic, with global->LDS loads
+//     (global_load_lds_dwordx4: 1 KiB per instruction, no VGPRs).  The K, Q and V tiles are only
+//     read in phase 1, so their 2-deep ring slot is refilled with the tiles of chunk c + 2 right
+//     after b1 of chunk c; the record (T' hi/lo, P, decays), read until phase 3, has a 3-deep
+//     ring refilled two chunks ahead.  Every load thus has well over a chunk to land, from L2:
+//     a ninth wave pulls every line into L2 six chunks ahead of use, with loads it never waits
+//     for, since a miss to HBM takes longer than a chunk.  The producers also write the output
+//     rows that the compute waves leave in LDS.
+//   * Each producer wave's loads are a fixed share, spread over the barrier intervals: a CU's
+//     vector memory unit moves well under 64 B per clock, so a wave issuing a whole chunk at once
+//     stalls (and holds up the next barrier), and a compute wave touching global memory would
+//     wait behind the producers' queue.  The compute waves do no global access in the chunk loop.
+//   * The compute waves read every operand from LDS (K^T fragments come from the K tile through
+//     transposing LDS reads); LDS also carries the three cross-wave exchanges per chunk: bf16 H,
+//     R and U~.
 #include "gdn_device.h"
 
 namespace gdn {
 
 namespace {
 
-constexpr int kPitchH = kDim + 8;     // Ht row pitch (bf16): value column j, key index
-constexpr int kPitchT = kChunk + 8;   // Rh/Rl/Uh/Ul/Uo row pitch (bf16): value column j, token
+constexpr int kHtBytes = kDvTile * kDim * 2;    // bf16 H exchange buffer
+constexpr int kXBytes = kDvTile * kChunk * 2;    // R / U~ exchange buffers
 constexpr int kComputeWaves = 4;
-constexpr int kThreads = 64 * (kComputeWaves + 1);
-constexpr int kStages = 3;
-// One ring stage: K tile (64 x 128 bf16, swizzled) | the v-head record | V tile (64 x 16 bf16).
-constexpr int kStK = 0;
-constexpr int kStRec = kStK + kChunk * kDim * 2;         // 16384
-constexpr int kStV = kStRec + kRecBytes;                  // 35328
-constexpr int kStageBytes = kStV + kChunk * kDvTile * 2;  // 37376
-constexpr int kDmaK = kChunk * kDim * 2 / 1024;           // 16 instructions of 1 KiB
+constexpr int kProducerWaves = 4;     // one per SIMD, beside one compute wave
+constexpr int kPrefetchWave = kComputeWaves + kProducerWaves;
+constexpr int kThreads = 64 * (kPrefetchWave + 1);
+constexpr int kPrefetchAhead = 6;     // chunks between the L2 warm-up of a chunk and its use
+// Tile ring slot: K tile | Q tile (64 x 128 bf16 each, swizzled) | V tile (64 x 16 bf16).
+constexpr int kTileStages = 2;
+constexpr int kTK = 0;
+constexpr int kTQ = kTK + kChunk * kDim * 2;              // 16384
+constexpr int kTV = kTQ + kChunk * kDim * 2;              // 32768
+constexpr int kTileBytes = kTV + kChunk * kDvTile * 2;    // 34816
+constexpr int kRecStages = 3;                             // record ring slot: kRecBytes
+constexpr int kOBytes = 16 * kDvTile * 2;                 // one compute wave's 16 output rows
+constexpr int kDmaTile = kChunk * kDim * 2 / 1024;        // 16 instructions of 1 KiB (K or Q)
 constexpr int kDmaRec = (kRecBytes + 1023) / 1024;        // 19 (the last one half full)
 constexpr int kDmaV = kChunk * kDvTile * 2 / 1024;        // 2
-constexpr int kDmaPerChunk = kDmaK + kDmaRec + kDmaV;     // 37
-constexpr int kTouchQ = 2;                                // L2 pulls of one chunk's Q rows
-static_assert(kStageBytes % 16 == 0 && kStRec % 16 == 0 && kStV % 16 == 0, "16-byte LDS slots");
+static_assert(kTileBytes % 16 == 0 && kRecBytes % 16 == 0 && kTV % 16 == 0, "16-byte LDS slots");
 
 // Byte offset of bf16 element (row, col) in a swizzled 64 x 128 tile: 16-byte chunks are
 // XOR-permuted by row so that 16 lanes reading one chunk column of 16 rows hit distinct banks.
@@ -54,10 +69,30 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * (kDim * 2) + ((((col >> 3) ^ (row & 15))) << 4) + ((col & 7) << 1);
 }
 
+// Value-major exchange buffers (16 value columns x n keys or tokens, bf16) are stored chunk-major:
+// the 16-byte chunk holding entries 8c .. 8c + 7 of column j sits at byte 16 (16 c + j).  A lane
+// group reading one chunk of columns 0..15 (an MFMA B operand) then touches 256 contiguous bytes,
+// which the LDS serves without bank conflicts (padded column-major rows conflict 4-way).
+__device__ __forceinline__ int vmaj(int j, int e) { return 16 * (16 * (e >> 3) + j) + 2 * (e & 7); }
+
+// State rows held by compute wave w: accumulator a, C-layout row i (0..15) is key
+// 8 (w + 8 a) + i for i < 8 and 8 (w + 8 a + 4) + i - 8 for i >= 8.  Taking the two 8-key
+// chunks of a K^T fragment 4 chunks apart keeps its transposing reads free of bank conflicts
+// under the row swizzle of the K tile; every wave still owns 32 keys and the 4 waves all 128.
+__device__ __forceinline__ int state_key(int w, int a, int i) {
+  return 8 * (w + 8 * a + 4 * (i >> 3)) + (i & 7);
+}
+
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane (M0 holds the wave's
 // LDS base).  Completion is tracked by this wave's vmcnt only.
 __device__ __forceinline__ void dma16(const void *src, unsigned lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset, so that
+// moving to the next chunk costs scalar adds only.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory");
 }
 // 4 bytes per lane into a scratch LDS word: pulls the 128-byte line holding src into L2.
 __device__ __forceinline__ void touch(const void *src, unsigned lds) {
@@ -79,7 +114,7 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint3
   hi = pack_bf16x2(a, b);
   lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
-__device__ __forceinline__ void store_u32x2(unsigned short *dst, uint32_t a, uint32_t b) {
+__device__ __forceinline__ void store_u32x2(void *dst, uint32_t a, uint32_t b) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   *reinterpret_cast<u32x2 *>(dst) = u32x2{a, b};
 }
@@ -93,80 +128,178 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const void *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
 }
 
-// Producer: one chunk's K tile, record and V tile into a ring stage (kDmaPerChunk instructions,
-// issued unconditionally so the vmcnt bookkeeping is static; rows past the sequence end are
-// clamped to its last row, which the compute waves never use).
-__device__ __forceinline__ void dma_chunk(int c, int tb, int te, int slot0, int hk, int h, int Hk,
-                                          int Hv, int d0, int l, const unsigned short *k,
-                                          const unsigned short *v, const uint8_t *rec,
-                                          unsigned stage_lds) {
+// Producers.  Per chunk the four producer waves issue the K and Q tiles (16 instructions each),
+// the record (19, the last one half full) and the V tile (2).  Wave pw's share is fixed -- tile
+// rows 4m .. 4m + 3 and record KiB m for m = pw mod 4, and the V tile on wave 3 -- so the vmcnt
+// bookkeeping is static.  Rows past the sequence end are clamped to its last row, which the
+// compute waves never use.
+__host__ __device__ constexpr int kRecA(int pw) { return 2; }                  // KiB pw, pw + 4
+__host__ __device__ constexpr int kRecB(int pw) { return pw < 3 ? 3 : 2; }     // pw + 8, + 12, + 16
+__host__ __device__ constexpr int kTileCount(int pw) { return 8 + (pw == 3 ? kDmaV : 0); }
+__host__ __device__ constexpr int kChunkCount(int pw) { return kRecA(pw) + kRecB(pw) + kTileCount(pw); }
+static_assert(kChunkCount(0) + kChunkCount(1) + kChunkCount(2) + kChunkCount(3) ==
+                  2 * kDmaTile + kDmaRec + kDmaV, "every load has an owner");
+
+// Per-lane byte offsets of a producer wave's loads, fixed for the whole sequence.  Tile
+// instruction i of wave pw covers tile rows 16 i + 4 pw .. + 3 (lane l: row 16 i + 4 pw + l / 16,
+// logical 16-byte chunk (l % 16) ^ (row % 16), stored at physical chunk l % 16); the row part
+// 16 i and the chunk's first token go into the scalar base.  V instruction m (wave 3) covers
+// rows 32 m + l / 2, 8 columns each.
+struct ProducerLanes {
+  uint32_t tile;  // (4 pw + l / 16) * row stride + 16 * lc
+  uint32_t v;     // (l / 2) * Hv * 256 + 2 * (d0 + 8 (l % 2))
+  uint32_t rec;   // 16 l
+  int lc, row0;   // for the clamped last chunk
+};
+
+// K, Q and V tiles of chunk c into a tile ring slot (kTileCount(pw) instructions).  kb, qb and vb
+// point at row 0 of this workgroup's head in bytes; rows past the sequence end are clamped to its
+// last row, which the compute waves never use.
+__device__ __forceinline__ void dma_tiles(int c, int tb, int te, int Hk, int Hv, int pw, int l,
+                                          const unsigned char *kb, const unsigned char *qb,
+                                          const unsigned char *vb, const ProducerLanes &pl,
+                                          unsigned slot) {
   const int t0 = tb + kChunk * c;
-  const int Lm1 = min(kChunk, te - t0) - 1;
+  const int L = min(kChunk, te - t0);
+  const size_t rs = (size_t)Hk * kDim * 2, vrs = (size_t)Hv * kDim * 2;
+  const unsigned char *kc = kb + (size_t)t0 * rs, *qc = qb + (size_t)t0 * rs, *vc = vb + (size_t)t0 * vrs;
+  if (L == kChunk) {
 #pragma unroll
-  for (int m = 0; m < kDmaK; ++m) {
-    const int row = 4 * m + (l >> 4);
-    const int lc = (l & 15) ^ (row & 15);  // logical 16-byte chunk stored at physical chunk l & 15
-    dma16(k + ((size_t)(t0 + min(row, Lm1)) * Hk + hk) * kDim + lc * 8, stage_lds + kStK + m * 1024);
-  }
-  const uint8_t *rp = rec + ((size_t)(slot0 + c) * Hv + h) * kRecBytes + l * 16;
+    for (int i = 0; i < 4; ++i) dma16s(kc + 16 * i * rs, pl.tile, slot + kTK + (4 * i + pw) * 1024);
 #pragma unroll
-  for (int m = 0; m < kDmaRec - 1; ++m) dma16(rp + m * 1024, stage_lds + kStRec + m * 1024);
-  if (l < (kRecBytes - (kDmaRec - 1) * 1024) / 16)
-    dma16(rp + (kDmaRec - 1) * 1024, stage_lds + kStRec + (kDmaRec - 1) * 1024);
+    for (int i = 0; i < 4; ++i) dma16s(qc + 16 * i * rs, pl.tile, slot + kTQ + (4 * i + pw) * 1024);
+    if (pw == 3) {
 #pragma unroll
-  for (int m = 0; m < kDmaV; ++m) {
-    const int row = 32 * m + (l >> 1);
-    dma16(v + ((size_t)(t0 + min(row, Lm1)) * Hv + h) * kDim + d0 + 8 * (l & 1),
-          stage_lds + kStV + m * 1024);
+      for (int m = 0; m < kDmaV; ++m) dma16s(vc + 32 * m * vrs, pl.v, slot + kTV + m * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (uint32_t)min(pl.row0 + 16 * i, L - 1) * (uint32_t)rs + 16 * pl.lc;
+      dma16s(kc, off, slot + kTK + (4 * i + pw) * 1024);
+      dma16s(qc, off, slot + kTQ + (4 * i + pw) * 1024);
+    }
+    if (pw == 3) {
+#pragma unroll
+      for (int m = 0; m < kDmaV; ++m) {
+        const uint32_t off = (uint32_t)min(32 * m + (l >> 1), L - 1) * (uint32_t)vrs + (pl.v % (uint32_t)vrs);
+        dma16s(vc, off, slot + kTV + m * 1024);
+      }
+    }
   }
 }
 
-__device__ __forceinline__ void touch_q(int c, int tb, int te, int hk, int Hk, int l,
-                                        const unsigned short *q, unsigned sink) {
-  const int t0 = tb + kChunk * c;
-  const unsigned short *qr = q + ((size_t)(t0 + min(l, min(kChunk, te - t0) - 1)) * Hk + hk) * kDim;
-  touch(qr, sink);
-  touch(qr + 64, sink);
+// Record of chunk slot `slot_idx` into a record ring slot: part A is KiB pw and pw + 4, part B
+// KiB pw + 8, pw + 12 and, below 19, pw + 16 (KiB 18 is half full).
+template <int Part>
+__device__ __forceinline__ void dma_rec(int64_t slot_idx, int h, int Hv, int pw, int l,
+                                        const uint8_t *rec, const ProducerLanes &pl,
+                                        unsigned slot) {
+  const uint8_t *rp = rec + ((size_t)slot_idx * Hv + h) * kRecBytes;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = kProducerWaves * (2 * Part + i) + pw;
+    dma16s(rp + m * 1024, pl.rec, slot + m * 1024);
+  }
+  if (Part == 1 && pw < 3) {
+    const int m = 16 + pw;
+    if (m < kDmaRec - 1 || l < (kRecBytes - (kDmaRec - 1) * 1024) / 16)
+      dma16s(rp + m * 1024, pl.rec, slot + m * 1024);
+  }
 }
 
-// Compute waves: Q rows 16w + (l%16) (clamped) as the A operands of Q H, one chunk ahead.
-__device__ __forceinline__ void load_q(bf16x8 (&qx)[4], int c, int tb, int te, int hk, int Hk, int w,
-                                       int l, const unsigned short *__restrict__ q) {
-  const int t0 = tb + kChunk * c;
-  const int row = min(16 * w + (l & 15), min(kChunk, te - t0) - 1);
-  const unsigned short *qr = q + ((size_t)(t0 + row) * Hk + hk) * kDim + 8 * (l >> 4);
+// L2 warm-up: one 4-byte load per 128-byte line.  The lines that the producers of all
+// workgroups sharing them will load -- the K and Q tiles (shared by the r = Hv / Hk heads of a
+// k-head and their 8 column slices), the v-head's record and V rows (shared by its 8 slices) --
+// are dealt out to those workgroups, so that each line is pulled once per L2.  gi is this
+// workgroup's index among the ng = 8 r sharing the k-head.  Lane slot s = 64 j + l of touch
+// instruction j names one line of chunk 0 (ptr) and the distance to the same line of the next
+// chunk (adv); inactive slots have ptr = nullptr.
+struct PrefetchLane {
+  const unsigned char *ptr[2];
+  uint32_t adv[2];
+};
+__device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, int hk, int h, int Hk,
+                                                       int Hv, int tile, int gi, int ng, int l,
+                                                       const unsigned short *q,
+                                                       const unsigned short *k,
+                                                       const unsigned short *v,
+                                                       const uint8_t *rec) {
+  PrefetchLane pf;
+  const int nkq = 4 * kChunk / ng;                   // K and Q lines: 64 rows x 2 lines each
+  const int nrec = (kRecBytes / 128 - tile + 7) / 8;  // record lines tile, tile + 8, ...
+  constexpr int nv = 2 * kChunk / kDvTiles;           // V lines: 64 rows x 2 lines (256 B a row)
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qx[ks] = load_bf16x8(qr + 32 * ks);
+  for (int j = 0; j < 2; ++j) {
+    int s = 64 * j + l;
+    pf.ptr[j] = nullptr;
+    pf.adv[j] = 0;
+    if (s < nkq) {
+      const int m = gi + ng * s;
+      const unsigned short *base = (m >> 7) ? q : k;
+      pf.ptr[j] = reinterpret_cast<const unsigned char *>(
+                      base + ((size_t)(tb + ((m >> 1) & 63)) * Hk + hk) * kDim) + 128 * (m & 1);
+      pf.adv[j] = (uint32_t)(kChunk * Hk * kDim * 2);
+    } else if ((s -= nkq) < nrec) {
+      pf.ptr[j] = rec + ((size_t)slot0 * Hv + h) * kRecBytes + 128 * (tile + 8 * s);
+      pf.adv[j] = (uint32_t)(Hv * kRecBytes);
+    } else if ((s -= nrec) < nv) {
+      const int m = tile + kDvTiles * s;
+      pf.ptr[j] = reinterpret_cast<const unsigned char *>(
+                      v + ((size_t)(tb + (m >> 1)) * Hv + h) * kDim) + 128 * (m & 1);
+      pf.adv[j] = (uint32_t)(kChunk * Hv * kDim * 2);
+    }
+  }
+  return pf;
+}
+
+// Output rows 16 pw .. 16 pw + 15 of chunk c, left by compute wave pw in its staging slot (rows
+// 4 g .. 4 g + 3 of column j at byte 8 (16 g + j)), to global memory.  One transposing read gives
+// lane i of lane group g row 4 g + i % 4, columns 4 (i / 4) .. + 3: lane r of the group names
+// column 4 (r % 4) + r / 4, rows 4 g .. 4 g + 3 (see lds_read_tr16).  ob points at column d0 of
+// this head in row 0 (bytes); ooff = row * Hv * 256 + 8 (i / 4) is the lane's fixed offset.
+__device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, int l,
+                                        const unsigned char *slot, unsigned char *ob, uint32_t ooff) {
+  const int g = l >> 4, i = l & 15;
+  const int col = 4 * (i & 3) + (i >> 2);
+  const v4i16 val = lds_read_tr16(slot + 8 * (16 * g + col));
+  const int t0 = tb + kChunk * c;
+  if (16 * pw + 4 * g + (i & 3) < min(kChunk, te - t0)) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2 *>(ob + (size_t)t0 * Hv * kDim * 2 + ooff) = __builtin_bit_cast(u32x2, val);
+  }
 }
 
 // One chunk on the compute waves.  Rows past the sequence end hold clamped data; they need no
 // masking because T' has zero rows and columns there (beta = 0), so U~ is zero on them, and
-// their output rows are never stored.
-__device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8 (&qx)[4], int t0,
-                                           int te, int h, int Hv, int d0, int w, int l,
-                                           f32x4 (&H)[2], unsigned short *Ht, unsigned short *Rh,
-                                           unsigned short *Rl, unsigned short *Uh,
-                                           unsigned short *Ul, unsigned short *Uo,
-                                           unsigned short *__restrict__ o) {
+// their output rows are never stored.  The chunk's K, Q and V tiles are in tile ring slot TS,
+// its record in record ring slot RS (compile-time, so that the slot offsets fold into the LDS
+// instructions); oslot is this wave's output staging slot.
+template <int TS, int RS>
+__device__ __forceinline__ void chunk_step(const unsigned char *tiles, const unsigned char *recs,
+                                           int w, int l, f32x4 (&H)[2], unsigned char *Ht,
+                                           unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
+                                           unsigned char *Ul, unsigned char *Uo,
+                                           unsigned char *oslot) {
   const int lj = l & 15, lg = l >> 4;
-  const int L = min(kChunk, te - t0);
-  const unsigned char *rs = st + kStRec;
+  const unsigned char *ts = tiles + TS * kTileBytes, *rs = recs + RS * kRecBytes;
+  const unsigned char *kt = ts + kTK, *qt = ts + kTQ;
 
-  // K^T fragments for the state update, read transposed from the K tile: fragment (key block
-  // 2w + a, token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][key 32 w + 16 a + lj].
+  // K^T fragments for the state update, read transposed from the K tile: fragment (accumulator
+  // a, token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][state_key(w, a, lj)].
   // ds_read_b64_tr_b16: within each 16-lane group, lane r names 4 consecutive bf16 (row r of a
   // 16 x 4 matrix M) and lane i receives M[4 j + i / 4][i % 4], j = 0..3.  With lane r = 4 j + q
-  // naming K[token t + j][key base + 4 q .. + 3], lane i receives K[t .. t + 3][base + i]: half a
-  // fragment (4 tokens) per read.
+  // naming K[token t + j][state_key(w, a, 4 q) .. + 3], lane i receives K[t .. t + 3] of key
+  // state_key(w, a, i): half a fragment (4 tokens) per read.
   bf16x8 kc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int key = 32 * w + 16 * a + 4 * (lj & 3);
+      const int key = state_key(w, a, 4 * (lj & 3));
       const int tok = 32 * ks + 8 * lg + (lj >> 2);
-      const v4i16 lo4 = lds_read_tr16(st + kStK + swz(tok, key));
-      const v4i16 hi4 = lds_read_tr16(st + kStK + swz(tok + 4, key));
+      const v4i16 lo4 = lds_read_tr16(kt + swz(tok, key));
+      const v4i16 hi4 = lds_read_tr16(kt + swz(tok + 4, key));
       kc[a][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
@@ -174,19 +307,23 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
   f32x4 X = zero4(), O = zero4();
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 hb = lds_bf16x8(&Ht[lj * kPitchH + 32 * ks + 8 * lg]);
-    const bf16x8 kx = lds_bf16x8(st + kStK + swz(16 * w + lj, 32 * ks + 8 * lg));
+    const bf16x8 hb = lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg));
+    const bf16x8 kx = lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 8 * lg));
+    const bf16x8 qx = lds_bf16x8(qt + swz(16 * w + lj, 32 * ks + 8 * lg));
     X = mfma_bf16(kx, hb, X);
-    O = mfma_bf16(qx[ks], hb, O);
+    O = mfma_bf16(qx, hb, O);
   }
   const f32x4 eg = *reinterpret_cast<const f32x4 *>(rs + kRecEG + (16 * w + 4 * lg) * 4);
   const f32x4 ed = *reinterpret_cast<const f32x4 *>(rs + kRecED + (16 * w + 4 * lg) * 4);
   const float egc = *reinterpret_cast<const float *>(rs + kRecEG + 63 * 4);
+  // V[16 w + 4 lg + rr][lj], rr = 0..3, in one transposing read: lane r of each lane group names
+  // row 16 w + 4 lg + r / 4, columns 4 (r % 4) .. + 3 of the row-major V tile.
   float vv[4];
+  {
+    const v4i16 v4 = lds_read_tr16(ts + kTV + ((16 * w + 4 * lg + (lj >> 2)) * kDvTile + 4 * (lj & 3)) * 2);
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-    vv[rr] = bits_to_float(*reinterpret_cast<const unsigned short *>(
-        st + kStV + ((16 * w + 4 * lg + rr) * kDvTile + lj) * 2));
+    for (int rr = 0; rr < 4; ++rr) vv[rr] = bits_to_float((unsigned short)v4[rr]);
+  }
 
   // R = V - e^G o X (hi/lo to LDS, value-major); O <- e^G o O
   {
@@ -199,8 +336,8 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
     uint32_t h0, l0, h1, l1;
     split_pair(R[0], R[1], h0, l0);
     split_pair(R[2], R[3], h1, l1);
-    store_u32x2(&Rh[lj * kPitchT + 16 * w + 4 * lg], h0, h1);
-    store_u32x2(&Rl[lj * kPitchT + 16 * w + 4 * lg], l0, l1);
+    store_u32x2(Rh + vmaj(lj, 16 * w + 4 * lg), h0, h1);
+    store_u32x2(Rl + vmaj(lj, 16 * w + 4 * lg), l0, l1);
   }
   __syncthreads();
 
@@ -210,16 +347,16 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
   {
     const bf16x8 th = lds_bf16x8(rs + kRecTpHi + fb * kFragBytes + l * 16);
     const bf16x8 tl = lds_bf16x8(rs + kRecTpLo + fb * kFragBytes + l * 16);
-    const bf16x8 bh = lds_bf16x8(&Rh[lj * kPitchT + 8 * lg]);
-    const bf16x8 bl = lds_bf16x8(&Rl[lj * kPitchT + 8 * lg]);
+    const bf16x8 bh = lds_bf16x8(Rh + vmaj(lj, 8 * lg));
+    const bf16x8 bl = lds_bf16x8(Rl + vmaj(lj, 8 * lg));
     U = mfma_bf16(th, bh, U);
     U = mfma_bf16(th, bl, U);
     U = mfma_bf16(tl, bh, U);
     if (w >= 2) {
       const bf16x8 th1 = lds_bf16x8(rs + kRecTpHi + (fb + 1) * kFragBytes + l * 16);
       const bf16x8 tl1 = lds_bf16x8(rs + kRecTpLo + (fb + 1) * kFragBytes + l * 16);
-      const bf16x8 bh1 = lds_bf16x8(&Rh[lj * kPitchT + 32 + 8 * lg]);
-      const bf16x8 bl1 = lds_bf16x8(&Rl[lj * kPitchT + 32 + 8 * lg]);
+      const bf16x8 bh1 = lds_bf16x8(Rh + vmaj(lj, 32 + 8 * lg));
+      const bf16x8 bl1 = lds_bf16x8(Rl + vmaj(lj, 32 + 8 * lg));
       U = mfma_bf16(th1, bh1, U);
       U = mfma_bf16(th1, bl1, U);
       U = mfma_bf16(tl1, bh1, U);
@@ -229,27 +366,23 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
     uint32_t h0, l0, h1, l1;
     split_pair(ed[0] * U[0], ed[1] * U[1], h0, l0);
     split_pair(ed[2] * U[2], ed[3] * U[3], h1, l1);
-    store_u32x2(&Uh[lj * kPitchT + 16 * w + 4 * lg], h0, h1);
-    store_u32x2(&Ul[lj * kPitchT + 16 * w + 4 * lg], l0, l1);
-    store_u32x2(&Uo[lj * kPitchT + 16 * w + 4 * lg], pack_bf16x2(U[0], U[1]),
-                pack_bf16x2(U[2], U[3]));
+    store_u32x2(Uh + vmaj(lj, 16 * w + 4 * lg), h0, h1);
+    store_u32x2(Ul + vmaj(lj, 16 * w + 4 * lg), l0, l1);
+    store_u32x2(Uo + vmaj(lj, 16 * w + 4 * lg), pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
   }
   __syncthreads();
 
   // o = e^G o (Q H) + P U~
   {
     O = mfma_bf16(lds_bf16x8(rs + kRecP + fb * kFragBytes + l * 16),
-                  lds_bf16x8(&Uo[lj * kPitchT + 8 * lg]), O);
+                  lds_bf16x8(Uo + vmaj(lj, 8 * lg)), O);
     if (w >= 2)
       O = mfma_bf16(lds_bf16x8(rs + kRecP + (fb + 1) * kFragBytes + l * 16),
-                    lds_bf16x8(&Uo[lj * kPitchT + 32 + 8 * lg]), O);
-    const uint32_t p01 = pack_bf16x2(O[0], O[1]), p23 = pack_bf16x2(O[2], O[3]);
-    const unsigned short ob[4] = {(unsigned short)p01, (unsigned short)(p01 >> 16),
-                                  (unsigned short)p23, (unsigned short)(p23 >> 16)};
-    unsigned short *orow = o + ((size_t)(t0 + 16 * w + 4 * lg) * Hv + h) * kDim + d0 + lj;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      if (16 * w + 4 * lg + rr < L) orow[(size_t)rr * Hv * kDim] = ob[rr];
+                    lds_bf16x8(Uo + vmaj(lj, 32 + 8 * lg)), O);
+    // staging slot: rows 4 lg .. 4 lg + 3 of column lj at byte 8 (16 lg + lj) = 8 l, so the
+    // write is lane-linear (the producers store it)
+    store_u32x2(reinterpret_cast<unsigned short *>(oslot + 8 * l), pack_bf16x2(O[0], O[1]),
+                pack_bf16x2(O[2], O[3]));
   }
 
   // H = e^{G_last} H + K^T (e^{G_last - G} o U~)  (decayed U~ hi + lo)
@@ -257,8 +390,8 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
   for (int a = 0; a < 2; ++a) H[a] *= egc;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 bh = lds_bf16x8(&Uh[lj * kPitchT + 32 * ks + 8 * lg]);
-    const bf16x8 bl = lds_bf16x8(&Ul[lj * kPitchT + 32 * ks + 8 * lg]);
+    const bf16x8 bh = lds_bf16x8(Uh + vmaj(lj, 32 * ks + 8 * lg));
+    const bf16x8 bl = lds_bf16x8(Ul + vmaj(lj, 32 * ks + 8 * lg));
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       H[a] = mfma_bf16(kc[a][ks], bh, H[a]);
@@ -267,7 +400,7 @@ __device__ __forceinline__ void chunk_step(const unsigned char *st, const bf16x8
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
-    store_u32x2(&Ht[lj * kPitchH + 32 * w + 16 * a + 4 * lg], pack_bf16x2(H[a][0], H[a][1]),
+    store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
                 pack_bf16x2(H[a][2], H[a][3]));
   __syncthreads();
 }
@@ -279,13 +412,15 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const float *h0, unsigned short *__restrict__ o, float *hT,  // hT may equal h0
     const uint8_t *__restrict__ rec, int Hk, int Hv) {
-  __shared__ __attribute__((aligned(16))) unsigned char ring[kStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned short Ht[kDvTile * kPitchH];
-  __shared__ __attribute__((aligned(16))) unsigned short Rh[kDvTile * kPitchT];
-  __shared__ __attribute__((aligned(16))) unsigned short Rl[kDvTile * kPitchT];
-  __shared__ __attribute__((aligned(16))) unsigned short Uh[kDvTile * kPitchT];
-  __shared__ __attribute__((aligned(16))) unsigned short Ul[kDvTile * kPitchT];
-  __shared__ __attribute__((aligned(16))) unsigned short Uo[kDvTile * kPitchT];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char recs[kRecStages * kRecBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Rh[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Uh[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Ul[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
   __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
 
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -294,36 +429,40 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   const int h = rest % Hv, n = rest / Hv;
   const int hk = h / (Hv / Hk);
   const int d0 = kDvTile * tile;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lj = l & 15, lg = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int tb = cu[n], te = cu[n + 1];
   const int nc = (te - tb + kChunk - 1) / kChunk;
   const int slot0 = tb / kChunk + n;
   const size_t state_base = ((size_t)n * Hv + h) * kDim * kDim;
 
-  if (w == kComputeWaves) {
-    // Producer wave.  Barriers: one before the loop, three per chunk, as the compute waves.
+  if (w == kPrefetchWave) {
+    // Prefetch wave: warms L2 kPrefetchAhead chunks ahead of use and never waits for its loads
+    // inside the loop (so a slow line holds up nothing).  Barriers as the compute waves.  A
+    // sequence's partial last chunk is not warmed (its rows past the end must not be read).
     if (nc > 0) {
-      const unsigned ring_lds = (unsigned)(uintptr_t)ring;
       const unsigned sink = (unsigned)(uintptr_t)touch_sink;
-      const bool lead = tile == 0 && (h % (Hv / Hk)) == 0;  // one Q-warming workgroup per k-head
-      if (lead)
-        for (int c = 0; c < 3; ++c) touch_q(min(c, nc - 1), tb, te, hk, Hk, l, q, sink);
-      dma_chunk(0, tb, te, slot0, hk, h, Hk, Hv, d0, l, k, v, rec, ring_lds);
-      dma_chunk(min(1, nc - 1), tb, te, slot0, hk, h, Hk, Hv, d0, l, k, v, rec,
-                ring_lds + kStageBytes);
-      wait_vmcnt<kDmaPerChunk>();  // chunk 0 has landed
+      const int r = Hv / Hk;
+      PrefetchLane pf = prefetch_lanes(tb, slot0, hk, h, Hk, Hv, tile, tile * r + h % r,
+                                       kDvTiles * r, l, q, k, v, rec);
+      const int nfull = (te - tb) / kChunk;  // chunks 0 .. nfull - 1 are full
+      // pointers of chunk 2
+#pragma unroll
+      for (int j = 0; j < 2; ++j) pf.ptr[j] += 2 * (size_t)pf.adv[j];
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
-        // Stage (c + 2) % 3 held chunk c - 1, which every compute wave finished before the last
-        // barrier; the clamped reload of the last chunk is never read.
-        if (lead) touch_q(min(c + 3, nc - 1), tb, te, hk, Hk, l, q, sink);
-        dma_chunk(min(c + 2, nc - 1), tb, te, slot0, hk, h, Hk, Hv, d0, l, k, v, rec,
-                  ring_lds + ((c + 2) % kStages) * kStageBytes);
+        // chunks 2 .. kPrefetchAhead - 1 at the first iteration, then chunk c + kPrefetchAhead
+        const int cbeg = c == 0 ? 2 : c + kPrefetchAhead;
+        const int cend = min(c + kPrefetchAhead, nfull - 1);
+        for (int cc = cbeg; cc <= cend; ++cc) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if (pf.ptr[j]) touch(pf.ptr[j], sink);
+            pf.ptr[j] += pf.adv[j];
+          }
+        }
         __syncthreads();
         __syncthreads();
-        // Chunk c + 1 must have landed before the end-of-chunk barrier: only this iteration's
-        // loads may still be in flight.
-        if (lead) wait_vmcnt<kDmaPerChunk + kTouchQ>(); else wait_vmcnt<kDmaPerChunk>();
         __syncthreads();
       }
     }
@@ -331,34 +470,92 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     return;
   }
 
-  // State slice: H[a][rr] = H[key 32w + 16a + 4 lg + rr][value d0 + lj].
+  if (w >= kComputeWaves) {
+    // Producer waves.  Barriers: one before the loop, three per chunk, as the compute waves.
+    const int pw = w - kComputeWaves;
+    if (nc > 0) {
+      const unsigned tiles_lds = (unsigned)(uintptr_t)tiles;
+      const unsigned recs_lds = (unsigned)(uintptr_t)recs;
+      const unsigned char *kb = reinterpret_cast<const unsigned char *>(k + (size_t)hk * kDim);
+      const unsigned char *qb = reinterpret_cast<const unsigned char *>(q + (size_t)hk * kDim);
+      const unsigned char *vb = reinterpret_cast<const unsigned char *>(v + (size_t)h * kDim);
+      unsigned char *ob = reinterpret_cast<unsigned char *>(o + (size_t)h * kDim + d0);
+      const unsigned char *oslot = ostage + pw * kOBytes;
+      ProducerLanes pl;
+      pl.row0 = 4 * pw + (l >> 4);
+      pl.lc = (l & 15) ^ (pl.row0 & 15);
+      pl.tile = (uint32_t)pl.row0 * (uint32_t)(Hk * kDim * 2) + 16 * pl.lc;
+      pl.v = (uint32_t)(l >> 1) * (uint32_t)(Hv * kDim * 2) + 2 * (d0 + 8 * (l & 1));
+      pl.rec = 16 * l;
+      const uint32_t ooff = (uint32_t)(16 * pw + 4 * (l >> 4) + (l & 3)) * (uint32_t)(Hv * kDim * 2) +
+                            8 * ((l & 15) >> 2);
+      const int c1 = min(1, nc - 1);
+      dma_tiles(0, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl, tiles_lds);
+      dma_rec<0>(slot0, h, Hv, pw, l, rec, pl, recs_lds);
+      dma_rec<1>(slot0, h, Hv, pw, l, rec, pl, recs_lds);
+      dma_tiles(c1, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl, tiles_lds + kTileBytes);
+      dma_rec<0>(slot0 + c1, h, Hv, pw, l, rec, pl, recs_lds + kRecBytes);
+      dma_rec<1>(slot0 + c1, h, Hv, pw, l, rec, pl, recs_lds + kRecBytes);
+      // chunk 0 has landed: only chunk 1's loads may still be in flight
+      if (pw == 3) wait_vmcnt<kChunkCount(3)>(); else wait_vmcnt<kChunkCount(0)>();
+      __syncthreads();
+      for (int c = 0; c < nc; ++c) {
+        // Chunk c + 2 is loaded during chunk c (clamped reloads of the last chunk only go to
+        // slots that are no longer read).  Its record slot (c + 2) % 3 held chunk c - 1, done
+        // before the last barrier; its tile slot c % 2 holds chunk c's tiles, done after b1.
+        const int cn = min(c + 2, nc - 1);
+        const unsigned rslot = recs_lds + ((c + 2) % kRecStages) * kRecBytes;
+        if (c > 0) store_o(c - 1, tb, te, Hv, pw, l, oslot, ob, ooff);
+        dma_rec<0>(slot0 + cn, h, Hv, pw, l, rec, pl, rslot);
+        __syncthreads();  // b1
+        dma_tiles(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl,
+                  tiles_lds + (c % kTileStages) * kTileBytes);
+        __syncthreads();  // b2
+        dma_rec<1>(slot0 + cn, h, Hv, pw, l, rec, pl, rslot);
+        // Chunk c + 1 (loaded during chunk c - 1) must have landed before b3: loads complete in
+        // issue order, so it is enough that at most this iteration's loads are in flight.
+        if (pw != 3) wait_vmcnt<kChunkCount(0)>(); else wait_vmcnt<kChunkCount(3)>();
+        __syncthreads();  // b3
+      }
+      store_o(nc - 1, tb, te, Hv, pw, l, oslot, ob, ooff);
+    }
+    wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
+    return;
+  }
+
+  // State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].
   f32x4 H[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int key = 32 * w + 16 * a + 4 * lg + rr;
+      const int key = state_key(w, a, 4 * lg + rr);
       H[a][rr] = h0 ? h0[state_base + (size_t)key * kDim + d0 + lj] : 0.f;
     }
 
   if (nc > 0) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
-      store_u32x2(&Ht[lj * kPitchH + 32 * w + 16 * a + 4 * lg], pack_bf16x2(H[a][0], H[a][1]),
+      store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
                   pack_bf16x2(H[a][2], H[a][3]));
-    bf16x8 qa[4], qb[4];
-    load_q(qa, 0, tb, te, hk, Hk, w, l, q);
     __syncthreads();
-    for (int c = 0; c < nc; c += 2) {
-      load_q(qb, min(c + 1, nc - 1), tb, te, hk, Hk, w, l, q);
-      chunk_step(ring + (c % kStages) * kStageBytes, qa, tb + kChunk * c, te, h, Hv, d0, w, l, H,
-                 Ht, Rh, Rl, Uh, Ul, Uo, o);
-      if (c + 1 < nc) {
-        load_q(qa, min(c + 2, nc - 1), tb, te, hk, Hk, w, l, q);
-        chunk_step(ring + ((c + 1) % kStages) * kStageBytes, qb, tb + kChunk * (c + 1), te, h, Hv,
-                   d0, w, l, H, Ht, Rh, Rl, Uh, Ul, Uo, o);
-      }
+    // six chunks per trip, so that every chunk's ring slots (c % 2, c % 3) are compile-time
+    unsigned char *oslot = ostage + w * kOBytes;
+#define GDN_STEP(ts, rs) chunk_step<ts, rs>(tiles, recs, w, l, H, Ht, Rh, Rl, Uh, Ul, Uo, oslot)
+    for (int c = 0; c < nc; c += 6) {
+      GDN_STEP(0, 0);
+      if (c + 1 == nc) break;
+      GDN_STEP(1, 1);
+      if (c + 2 == nc) break;
+      GDN_STEP(0, 2);
+      if (c + 3 == nc) break;
+      GDN_STEP(1, 0);
+      if (c + 4 == nc) break;
+      GDN_STEP(0, 1);
+      if (c + 5 == nc) break;
+      GDN_STEP(1, 2);
     }
+#undef GDN_STEP
   }
 
   if (hT) {
@@ -366,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int key = 32 * w + 16 * a + 4 * lg + rr;
+        const int key = state_key(w, a, 4 * lg + rr);
         hT[state_base + (size_t)key * kDim + d0 + lj] = H[a][rr];
       }
   }
