@@ -2,12 +2,20 @@
 """Benchmark of the chunked Gated DeltaNet prefill forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --copy-mib M [--workload NAME]
+
 
 A step is one gdn_chunk_fwd over one batch of synthetic inputs already resident in HBM (for the
 mixer workload: 48 back-to-back gdn_mixer_fwd layers).  Prints ONE JSON line with tokens/s per
 layer, the roofline of the dominant kernel (timed with HIP events on the launch stream, in a
 separate stage-by-stage loop), the whole-path roofline, and the fp64 CPU oracle timed on the host
 as a baseline.
+
+The second form turns two rocprofv3 counter runs of the first form (one with --pmc FETCH_SIZE,
+one with --pmc WRITE_SIZE, both with --copy-mib M) into profiles/traffic_<kernel>_<workload>.json:
+the counters of the dominant kernel per dispatch, each scaled by what the same counter reads for a
+plain device copy of M MiB, and a hash of the kernel's sources.  A later bench run reports that
+traffic in roofline.traffic only while the hash still matches.
 
 Workloads (seeded, synthetic; see gdn_inputs.py):
     t539_h16x32      single sequence, T=539, Hk=16, Hv=32, d=128  (default)
@@ -75,6 +83,91 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ------------------------------------------------------------------------------------------------
+# Measured HBM traffic of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE)
+# ------------------------------------------------------------------------------------------------
+KERNEL_SOURCES = {
+    "state_pass": ["gated_deltanet_chunked_amd/csrc/state_pass.hip", "gated_deltanet_chunked_amd/csrc/gdn_device.h"],
+    "chunk_prep": ["gated_deltanet_chunked_amd/csrc/chunk_prep.hip", "gated_deltanet_chunked_amd/csrc/gdn_device.h"],
+}
+KERNEL_SYMBOLS = {"state_pass": "state_pass_kernel", "chunk_prep": "chunk_prep_kernel"}
+
+
+def kernel_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+
+
+def read_counter(run_dir, counter):
+    """Per-dispatch sums of `counter` (KiB) by kernel name, from a rocprofv3 csv run directory."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), v in per.items():
+        by_kernel.setdefault(name, []).append(v)
+    return by_kernel
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_mib, workload):
+    out = {"workload": workload, "copy_mib": copy_mib}
+    copy_bytes = copy_mib * 2 ** 20
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        by_kernel = read_counter(run_dir, counter)
+        # the calibration copy: the three largest dispatches of kernels whose name says they copy
+        # (input uploads share the kernel name but are far smaller than the copy)
+        copies = sorted((v for n, vs in by_kernel.items() if "copy" in n.lower() for v in vs), reverse=True)[:3]
+        if not copies:
+            raise SystemExit(f"no copy kernel found in {run_dir}")
+        copy_kib = statistics.median(copies)
+        calib = copy_bytes / (copy_kib * 1024.0)
+        out[counter] = {"copy_kib": copy_kib, "bytes_per_counted_byte": calib, "kernels": {}}
+        for kern, sym in KERNEL_SYMBOLS.items():
+            vals = [v for n, vs in by_kernel.items() if sym in n for v in vs]
+            if vals:
+                out[counter]["kernels"][kern] = {"dispatches": len(vals), "kib_median": statistics.median(vals),
+                                                 "bytes_per_launch": statistics.median(vals) * 1024.0 * calib}
+    for kern in KERNEL_SYMBOLS:
+        if kern in out["FETCH_SIZE"]["kernels"] and kern in out["WRITE_SIZE"]["kernels"]:
+            rec = {"kernel": kern, "workload": workload, "src_sha": kernel_sha(kern),
+                   "fetch_bytes": round(out["FETCH_SIZE"]["kernels"][kern]["bytes_per_launch"]),
+                   "write_bytes": round(out["WRITE_SIZE"]["kernels"][kern]["bytes_per_launch"]),
+                   "fetch_calibration": out["FETCH_SIZE"]["bytes_per_counted_byte"],
+                   "write_calibration": out["WRITE_SIZE"]["bytes_per_counted_byte"],
+                   "dispatches": [out["FETCH_SIZE"]["kernels"][kern]["dispatches"],
+                                  out["WRITE_SIZE"]["kernels"][kern]["dispatches"]]}
+            rec["traffic_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+            with open(traffic_path(kern, workload), "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+            log(f"[bench] {kern}: {rec['traffic_bytes'] / 1e6:.2f} MB per launch -> {traffic_path(kern, workload)}")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
+    try:
+        with open(traffic_path(kernel, workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return rec["traffic_bytes"] if rec.get("src_sha") == kernel_sha(kernel) else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,7 +180,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on oracle time for the baseline")
     ap.add_argument("--copy-mib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_*.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        if args.copy_mib <= 0:
+            raise SystemExit("--summarize-traffic needs the --copy-mib the runs used")
+        summarize_traffic(*args.summarize_traffic, args.copy_mib, args.workload)
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -192,7 +293,8 @@ def main():
         dominant = max(stages, key=lambda k: stages[k]["us_mean"])
         dom = stages[dominant]
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dominant, args.workload),
                     "bytes_per_launch": dom["bytes"], "us_per_launch": round(dom["us_mean"], 3)}
         pb, pf = path_bytes(T, N, Hk, Hv, with_h0), path_flops(T, Hk, Hv)
     else:
