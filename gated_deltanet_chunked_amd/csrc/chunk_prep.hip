@@ -6,17 +6,20 @@
 // side while only the state is passed in sequence.  This kernel does all of that state-independent
 // work for every (chunk, v-head) at once; the sequential part lives in state_pass.hip.
 //
-// One workgroup (4 waves) per (chunk slot, v-head h), k-head hk = h / (Hv / Hk):
-//   1. G = inclusive cumsum of g over the chunk (a wave64 scan: 64 tokens = 64 lanes).
-//   2. K K^T and Q K^T over the lower 16x16 block triangle on bf16 MFMA (fp32 accumulate); the
-//      decayed, masked products are formed straight from the accumulators:
-//        A_ij = beta_i e^{G_i - G_j} (k_i . k_j)  for i > j       (fp32, LDS)
-//        P_ij = e^{G_i - G_j} (q_i . k_j)         for i >= j      (fp32, LDS)
-//   3. T = (I + A)^-1: each 16x16 diagonal block by right-looking substitution (one column per
-//      lane), then the off-diagonal blocks by T_ij = -T_ii sum_m A_im T_mj on fp32 MFMA, one
-//      sub-diagonal at a time.
-//   4. T' = T diag(beta) as bf16 hi + lo MFMA fragments, P as bf16 fragments, e^{G} and
-//      e^{G_last - G} -> the record the state pass reads.
+// One workgroup per (chunk slot, HP = 1 or 2 v-heads of one k-head), 4 waves per v-head.  Every
+// v-head of a k-head shares K K^T and Q K^T (only the decays and beta tell them apart), so a pair
+// of them shares the products and the q/k loads:
+//   1. G = inclusive cumsum of g over the chunk per v-head (a wave64 scan: 64 tokens = 64 lanes).
+//   2. S = K K^T and Q K^T over the lower 16x16 block triangle on bf16 MFMA (fp32 accumulate),
+//      each block computed transposed, so that a lane holds 4 consecutive columns of one row.
+//   3. From the accumulators, per v-head:
+//        A_ij = beta_i e^{G_i - G_j} (k_i . k_j)  for i > j      (fp32, LDS)
+//        P_ij = e^{G_i - G_j} (q_i . k_j)         for i >= j     (bf16, straight to the record)
+//   4. T = (I + A)^-1: each 16x16 diagonal block by right-looking substitution (one column per
+//      lane), then block column j by T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, with
+//      the column's blocks kept in registers, one wave per block column (no barrier in between).
+//   5. T' = T diag(beta) as bf16 hi + lo MFMA fragments, e^{G} and e^{G_last - G}: the rest of the
+//      record the state pass reads.
 // Every exponent is <= 0 (G is non-increasing), so no e^{-G} is ever formed.  Tokens past the
 // end of a sequence enter as k = q = 0, g = 0, beta = 0, which leaves T' and P zero on them.
 #include "gdn_device.h"
@@ -25,18 +28,23 @@ namespace gdn {
 
 namespace {
 
-constexpr int kPitchF = 68;                       // fp32 row pitch of 64 x 64 LDS matrices
-constexpr int kMatBytes = kChunk * kPitchF * 4;   // 17408
+constexpr int kPitchF = 68;                        // fp32 row pitch of 64 x 64 LDS matrices
+constexpr int kMatBytes = kChunk * kPitchF * 4;    // 17408
+constexpr int kMaxHeads = 2;                       // v-heads per workgroup
 // LDS map: [Ks | Qs] (bf16 64 x 128, swizzled) are dead once the products are in registers, so
-// [As | Ps] reuse their space; then Ts and beta.
+// the A matrices reuse their space; then the T matrices, then G and beta per v-head.
 constexpr int kOffKs = 0;
-constexpr int kOffQs = kChunk * kDim * 2;         // 16384
-constexpr int kOffAs = 0;
-constexpr int kOffPs = kMatBytes;
-constexpr int kOffTs = 2 * kMatBytes;
-constexpr int kOffB = kOffTs + kMatBytes;
-constexpr int kOffG = kOffB + kChunk * 4;
-constexpr int kLdsBytes = kOffG + kChunk * 4;     // 52736: three workgroups per CU
+constexpr int kOffQs = kChunk * kDim * 2;                  // 16384
+constexpr int kOffA = 0;                                   // + x * kMatBytes
+constexpr int kOffT = kMaxHeads * kMatBytes;               // 34816 + x * kMatBytes
+constexpr int kOffG = 2 * kMaxHeads * kMatBytes;           // 69632: G[x][64]
+constexpr int kOffB = kOffG + kMaxHeads * kChunk * 4;      // beta[x][64]
+constexpr int kLdsBytes = kOffB + kMaxHeads * kChunk * 4;  // 70656: two workgroups per CU
+static_assert(kMaxHeads * kMatBytes >= 2 * kChunk * kDim * 2, "the A matrices cover Ks and Qs");
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Byte offset of bf16 element (row, col) in a swizzled 64 x 128 tile: 16-byte chunks are
 // XOR-permuted by row so that 16 lanes reading one chunk column of 16 rows hit distinct banks.
@@ -46,6 +54,15 @@ __device__ __forceinline__ int swz(int row, int col) {
 
 // e^x for x <= 0 from the hardware 2^x (v_exp_f32): relative error about 1e-7 |x|.
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// hi = bf16(x), lo = bf16(x - hi) for two values at once (packed bf16 pairs).
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
 
 // Largest n in [0, N) with cu[n] / 64 + n <= slot (that map is increasing in n).  One round of
 // 64 lanes per 64 sequences; every wave runs it, results are wave-uniform.
@@ -62,24 +79,32 @@ __device__ __forceinline__ int find_sequence(const int32_t *__restrict__ cu, int
   return n;
 }
 
+// Record fragment holding row block rb, token step ks (see gdn_device.h).
+__device__ __forceinline__ int frag_index(int rb, int ks) { return rb < 2 ? rb : 2 * rb - 2 + ks; }
+
+// Lower-triangle block b (0..9) -> (row block, column block), column block <= row block.
+__device__ __forceinline__ int block_row(int b) { return b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3)); }
+
 }  // namespace
 
-__global__ __launch_bounds__(256) void chunk_prep_kernel(
+template <int HP>
+__global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec) {
+  constexpr int kThreads = 256 * HP, kWaves = 4 * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   unsigned char *Ks = smem + kOffKs;
   unsigned char *Qs = smem + kOffQs;
-  float *As = reinterpret_cast<float *>(smem + kOffAs);
-  float *Ps = reinterpret_cast<float *>(smem + kOffPs);
-  float *Ts = reinterpret_cast<float *>(smem + kOffTs);
-  float *Bs = reinterpret_cast<float *>(smem + kOffB);
-  float *Gs = reinterpret_cast<float *>(smem + kOffG);
+  float *Gall = reinterpret_cast<float *>(smem + kOffG);
+  float *Ball = reinterpret_cast<float *>(smem + kOffB);
 
-  const int slot = blockIdx.x, h = blockIdx.y;
-  const int r = Hv / Hk, hk = h / r;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lj = l & 15, lg = l >> 4;
+  const int slot = blockIdx.x;
+  const int h_first = blockIdx.y * HP, hk = h_first / (Hv / Hk);
+  const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = w >> 2, wl = w & 3;  // this wave's v-head within the group, wave within the head
+  const int h = h_first + hh;
 
   int tb = 0, te = T, n = 0;
   if (N > 1) {
@@ -91,175 +116,225 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
   const int t0 = tb + kChunk * c;
   if (t0 >= te) return;  // slot unused (uniform across the workgroup)
   const int L = min(kChunk, te - t0);
+  uint8_t *const rec_slot = rec + (size_t)slot * Hv * kRecBytes;  // v-head x at + x * kRecBytes
 
-  // ---- 1. issue every global load up front ------------------------------------------------
-  u32x4 kv[4], qv[4];
+  // ---- 1. global loads up front; gate cumsum per v-head --------------------------------------
+  constexpr int kIt = 1024 / kThreads;  // 16-byte pieces of one 64 x 128 tile per thread
+  u32x4 kv[kIt], qv[kIt];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int p = tid + 256 * it, row = p >> 4, ch = p & 15;
+  for (int it = 0; it < kIt; ++it) {
+    const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
     const size_t off = ((size_t)(t0 + min(row, L - 1)) * Hk + hk) * kDim + ch * 8;
     kv[it] = *reinterpret_cast<const u32x4 *>(k + off);
     qv[it] = *reinterpret_cast<const u32x4 *>(q + off);
   }
   const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
   const float g_raw = g[gi], b_raw = beta[gi];
-
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int p = tid + 256 * it, row = p >> 4, ch = p & 15;
+  for (int it = 0; it < kIt; ++it) {
+    const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const int so = row * (kDim * 2) + ((ch ^ (row & 15)) << 4);
     *reinterpret_cast<u32x4 *>(Ks + so) = row < L ? kv[it] : zero;
     *reinterpret_cast<u32x4 *>(Qs + so) = row < L ? qv[it] : zero;
   }
-  // Gate cumsum: every wave holds G and beta for all 64 tokens (lane = token).
   const float gv = l < L ? g_raw : 0.f;
   const float bv = l < L ? b_raw : 0.f;
   const float G = wave_inclusive_scan(gv);
   const float Glast = __shfl(G, 63, 64);
-  if (w == 0) {
-    Bs[l] = bv;
-    Gs[l] = G;
+  if (wl == 0) {
+    Gall[kChunk * hh + l] = G;
+    Ball[kChunk * hh + l] = bv;
+    uint8_t *R = rec_slot + (size_t)h * kRecBytes;
+    reinterpret_cast<float *>(R + kRecEG)[l] = exp_neg(G);
+    reinterpret_cast<float *>(R + kRecED)[l] = exp_neg(Glast - G);
   }
   __syncthreads();
 
-  // ---- 2. K K^T and Q K^T: 20 block products (lower triangle of each), 5 per wave ----------
-  f32x4 acc[5];
+  // ---- 2. block products, transposed: C[j][i] = sum_d K[j][d] X[i][d], X = K (p < 10) or Q ----
+  // Block b of the lower triangle is (row block rb, column block cb); accumulator lane (lj, lg)
+  // then holds S[i = 16 rb + lj][j = 16 cb + 4 lg + rr], rr = 0..3.
+  constexpr int kPer = (20 + kWaves - 1) / kWaves;
+  f32x4 acc[kPer];
 #pragma unroll
-  for (int it = 0; it < 5; ++it) {
-    const int p = w + 4 * it;
-    const int which = p >= 10 ? 1 : 0;
-    const int b = p - 10 * which;
-    const int rb = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3));
-    const int cb = b - rb * (rb + 1) / 2;
-    const unsigned char *Am = which ? Qs : Ks;
-    acc[it] = zero4();
+  for (int it = 0; it < kPer; ++it) {
+    const int p = w + kWaves * it;
+    if (p < 20) {
+      const int which = p >= 10 ? 1 : 0;
+      const int b = p - 10 * which;
+      const int rb = block_row(b), cb = b - rb * (rb + 1) / 2;
+      const unsigned char *Xm = which ? Qs : Ks;
+      acc[it] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = 4 * ks + lg;
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Am + swz(16 * rb + lj, ch * 8));
-      const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(Ks + swz(16 * cb + lj, ch * 8));
-      acc[it] = mfma_bf16(a, bb, acc[it]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ch = 4 * ks + lg;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Ks + swz(16 * cb + lj, ch * 8));
+        const bf16x8 bx = *reinterpret_cast<const bf16x8 *>(Xm + swz(16 * rb + lj, ch * 8));
+        acc[it] = mfma_bf16(a, bx, acc[it]);
+      }
     }
   }
-  __syncthreads();  // Ks, Qs are dead from here on; As, Ps take their space
+  __syncthreads();  // Ks, Qs are dead from here on; the A matrices take their space
 
-  // Decayed, masked products straight from the accumulators: lane (col lj, rows 4 lg + rr).
+  // ---- 3. A (fp32, LDS) and P (bf16 record fragments) for every v-head of the group -----------
+  // P's fragment k-slots follow the accumulators: fragment (rb, ks), lane (i, g) slot e holds
+  // P[i][32 ks + 16 (e / 4) + 4 g + e % 4], so block (rb, cb) fills bytes 8 (cb % 2) .. + 7 of each
+  // lane's 16 bytes, and the zero block beside a diagonal block is written as zeros.
+  // A's off-diagonal blocks are stored row-major; its diagonal blocks (read only by the
+  // substitution, which walks columns) are stored transposed: entry (o + a, o + b) holds A[o+b][o+a].
+  // A diagonal block of K K^T is symmetric, so the same accumulator gives both.
 #pragma unroll
-  for (int it = 0; it < 5; ++it) {
-    const int p = w + 4 * it;
-    const int which = p >= 10 ? 1 : 0;
-    const int b = p - 10 * which;
-    const int rb = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3));
-    const int cb = b - rb * (rb + 1) / 2;
-    const int j = 16 * cb + lj;
-    const int i0 = 16 * rb + 4 * lg;
-    const float Gj = Gs[j];
-    const f32x4 Gi = *reinterpret_cast<const f32x4 *>(&Gs[i0]);
-    const f32x4 Bi = *reinterpret_cast<const f32x4 *>(&Bs[i0]);
-    float *M = which ? Ps : As;
+  for (int it = 0; it < kPer; ++it) {
+    const int p = w + kWaves * it;
+    if (p < 20) {
+      const int which = p >= 10 ? 1 : 0;
+      const int b = p - 10 * which;
+      const int rb = block_row(b), cb = b - rb * (rb + 1) / 2;
+      const int i = 16 * rb + lj, j0 = 16 * cb + 4 * lg;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = i0 + rr;
-      const float d = exp_neg(Gi[rr] - Gj) * acc[it][rr];
-      M[i * kPitchF + j] = which ? (i >= j ? d : 0.f) : (i > j ? Bi[rr] * d : 0.f);
+      for (int x = 0; x < HP; ++x) {
+        const float *Gx = Gall + kChunk * x;
+        const float Gi = Gx[i];
+        const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gx + j0);
+        if (which) {
+          float d[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) d[rr] = j0 + rr <= i ? exp_neg(Gi - Gj[rr]) * acc[it][rr] : 0.f;
+          const u32x2 val = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
+          uint8_t *dst = rec_slot + (size_t)(h_first + x) * kRecBytes + kRecP +
+                         frag_index(rb, cb >> 1) * kFragBytes + l * 16 + 8 * (cb & 1);
+          if ((cb & 1) == 0 && cb + 1 > rb) {  // the other half is an upper block: zeros
+            const u32x4 v4 = {val[0], val[1], 0u, 0u};
+            *reinterpret_cast<u32x4 *>(dst) = v4;
+          } else {
+            *reinterpret_cast<u32x2 *>(dst) = val;
+          }
+        } else {
+          float *Ax = reinterpret_cast<float *>(smem + kOffA + x * kMatBytes);
+          f32x4 av;
+          if (rb != cb) {
+            const float bi = Ball[kChunk * x + i];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) av[rr] = bi * exp_neg(Gi - Gj[rr]) * acc[it][rr];
+          } else {
+            const f32x4 bj = *reinterpret_cast<const f32x4 *>(Ball + kChunk * x + j0);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              av[rr] = j0 + rr > i ? bj[rr] * exp_neg(Gj[rr] - Gi) * acc[it][rr] : 0.f;
+          }
+          *reinterpret_cast<f32x4 *>(Ax + i * kPitchF + j0) = av;
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---- 3. T = (I + A)^-1 ---------------------------------------------------------------------
-  // Diagonal block w, column cj = lane: right-looking substitution, so each step only waits for
-  // one multiply-add of the previous step.
+  // ---- 4. T = (I + A)^-1 for this wave's v-head ------------------------------------------------
+  const float *As = reinterpret_cast<const float *>(smem + kOffA + hh * kMatBytes);
+  float *Ts = reinterpret_cast<float *>(smem + kOffT + hh * kMatBytes);
+  // Diagonal block wl, column cj = lane: right-looking substitution (each step waits for one
+  // multiply-add of the previous one).  Step m needs column m of the block below the diagonal,
+  // which the transposed storage makes a contiguous row.
   if (l < 16) {
-    const int cj = l;
+    const int cj = l, o = 16 * wl;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = i == cj ? 1.f : 0.f;
 #pragma unroll
     for (int m = 0; m < 15; ++m) {
+      float a[16];
 #pragma unroll
-      for (int i = m + 1; i < 16; ++i) x[i] -= As[(16 * w + i) * kPitchF + 16 * w + m] * x[m];
+      for (int v4 = (m + 1) / 4; v4 < 4; ++v4) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(As + (o + m) * kPitchF + o + 4 * v4);
+        a[4 * v4] = t[0], a[4 * v4 + 1] = t[1], a[4 * v4 + 2] = t[2], a[4 * v4 + 3] = t[3];
+      }
+#pragma unroll
+      for (int i = m + 1; i < 16; ++i) x[i] -= a[i] * x[m];
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Ts[(16 * w + i) * kPitchF + 16 * w + cj] = x[i];
+    for (int i = 0; i < 16; ++i) Ts[(o + i) * kPitchF + o + cj] = x[i];
   }
   __syncthreads();
 
-  // Off-diagonal blocks, one sub-diagonal at a time: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.
+  // Block column j = wl: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj for i = j + 1 .. 3, with the
+  // column's blocks in registers (C layout: lane (col lj, rows 4 lg + rr)).  In every product the
+  // k-slot (step s, lane group lg) stands for row 4 lg + s of the B operand, so an accumulator is
+  // fed back as B without moving data between lanes.
+  {
+    const int j = wl;
+    f32x4 Tcol[4];  // Tcol[m] = T_mj for j < m < i
 #pragma unroll
-  for (int d = 1; d <= 3; ++d) {
-    if (w < 4 - d) {
-      const int bi = w + d, bj = w;
-      f32x4 S = zero4();
-      for (int m = bj; m < bi; ++m) {
+    for (int i = 1; i < 4; ++i) {
+      if (i > j) {
+        f32x4 S = zero4();
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const float a = As[(16 * bi + lj) * kPitchF + 16 * m + 4 * s4 + lg];
-          const float bb = Ts[(16 * m + 4 * s4 + lg) * kPitchF + 16 * bj + lj];
-          S = mfma_f32(a, bb, S);
+        for (int m = 0; m < 3; ++m) {
+          if (m >= j && m < i) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const float a = As[(16 * i + lj) * kPitchF + 16 * m + 4 * lg + s];
+              const float bb = m == j ? Ts[(16 * m + 4 * lg + s) * kPitchF + 16 * j + lj] : Tcol[m][s];
+              S = mfma_f32(a, bb, S);
+            }
+          }
+        }
+        f32x4 Tb = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float a = Ts[(16 * i + lj) * kPitchF + 16 * i + 4 * lg + s];
+          Tb = mfma_f32(a, S[s], Tb);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          Tcol[i][s] = -Tb[s];
+          Ts[(16 * i + 4 * lg + s) * kPitchF + 16 * j + lj] = -Tb[s];
         }
       }
-      // S is fed back as the B operand: k-slot (step rr, group lg) <-> row 4 lg + rr.
-      f32x4 Tb = zero4();
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float a = Ts[(16 * bi + lj) * kPitchF + 16 * bi + 4 * lg + rr];
-        Tb = mfma_f32(a, S[rr], Tb);
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Ts[(16 * bi + 4 * lg + rr) * kPitchF + 16 * bj + lj] = -Tb[rr];
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  // ---- 4. the record: T' = T diag(beta) hi/lo fragments, P fragments, decays ----------------
-  uint8_t *R = rec + ((size_t)slot * Hv + h) * kRecBytes;
-  if (w == 0) {
-    reinterpret_cast<float *>(R + kRecEG)[l] = exp_neg(G);
-    reinterpret_cast<float *>(R + kRecED)[l] = exp_neg(Glast - G);
-  }
-  for (int task = tid; task < 2 * kFrags * 64; task += 256) {
-    const int kind = task / (kFrags * 64);  // wave-uniform
-    const int rem = task - kind * kFrags * 64;
-    const int f = rem >> 6, ll = rem & 63;
+  // ---- 5. T' = T diag(beta) as bf16 hi/lo fragments -------------------------------------------
+  // Fragment f, lane ll: row i = 16 rb(f) + ll % 16, columns 32 ks(f) + 8 (ll / 16) .. + 7.
+  uint8_t *R = rec_slot + (size_t)h * kRecBytes;
+  const float *Bh = Ball + kChunk * hh;
+  for (int task = 64 * wl + l; task < kFrags * 64; task += 256) {
+    const int f = task >> 6, ll = task & 63;
     const int i = 16 * frag_row_block(f) + (ll & 15);
     const int c0 = 32 * frag_k_step(f) + 8 * (ll >> 4);
-    const float *row = (kind == 0 ? Ts : Ps) + i * kPitchF + c0;
-    const f32x4 m0 = *reinterpret_cast<const f32x4 *>(row);
-    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(row + 4);
-    const float mv[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-    if (kind == 0) {
-      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&Bs[c0]);
-      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&Bs[c0 + 4]);
-      const float bvv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      u16x8 vh, vl;
+    const f32x4 m0 = *reinterpret_cast<const f32x4 *>(Ts + i * kPitchF + c0);
+    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(Ts + i * kPitchF + c0 + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(Bh + c0);
+    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(Bh + c0 + 4);
+    float t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int cc = c0 + e;
-        const float t = (cc < i) ? mv[e] : (cc == i ? 1.f : 0.f);
-        __bf16 bh, bl;
-        split_hilo(t * bvv[e], bh, bl);
-        vh[e] = bf16_bits(bh);
-        vl[e] = bf16_bits(bl);
-      }
-      *reinterpret_cast<u16x8 *>(R + kRecTpHi + f * kFragBytes + ll * 16) = vh;
-      *reinterpret_cast<u16x8 *>(R + kRecTpLo + f * kFragBytes + ll * 16) = vl;
-    } else {
-      u16x8 vp;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vp[e] = bf16_bits(to_bf16(c0 + e <= i ? mv[e] : 0.f));
-      *reinterpret_cast<u16x8 *>(R + kRecP + f * kFragBytes + ll * 16) = vp;
+    for (int e = 0; e < 8; ++e) {
+      const int cc = c0 + e;
+      const float mv = e < 4 ? m0[e] : m1[e - 4];
+      const float bb = e < 4 ? b0[e] : b1[e - 4];
+      t[e] = cc < i ? mv * bb : (cc == i ? bb : 0.f);
     }
+    uint32_t hv[4], lv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_pair(t[2 * e], t[2 * e + 1], hv[e], lv[e]);
+    const u32x4 vh = {hv[0], hv[1], hv[2], hv[3]}, vl = {lv[0], lv[1], lv[2], lv[3]};
+    *reinterpret_cast<u32x4 *>(R + kRecTpHi + f * kFragBytes + ll * 16) = vh;
+    *reinterpret_cast<u32x4 *>(R + kRecTpLo + f * kFragBytes + ll * 16) = vl;
   }
 }
 
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
                        void *rec, hipStream_t stream) {
-  dim3 grid((unsigned)nslots, (unsigned)Hv);
-  hipLaunchKernelGGL(chunk_prep_kernel, grid, dim3(256), 0, stream,
-                     static_cast<const unsigned short *>(q), static_cast<const unsigned short *>(k),
-                     g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec));
+  const unsigned short *qp = static_cast<const unsigned short *>(q);
+  const unsigned short *kp = static_cast<const unsigned short *>(k);
+  uint8_t *rp = static_cast<uint8_t *>(rec);
+  if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
+    hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)nslots, (unsigned)(Hv / 2)), dim3(512), 0,
+                       stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
+  else
+    hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)nslots, (unsigned)Hv), dim3(256), 0,
+                       stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
 }
 
 }  // namespace gdn

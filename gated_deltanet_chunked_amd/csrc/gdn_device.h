@@ -34,7 +34,10 @@ constexpr int kFrags = 6;
 constexpr int kFragBytes = 64 * 16;                       // 64 lanes x 8 bf16
 constexpr int kRecTpHi = 0;                               // T' = (I+A)^-1 diag(beta), bf16 high part
 constexpr int kRecTpLo = kRecTpHi + kFrags * kFragBytes;  // T' low part (T' - hi rounded to bf16)
-constexpr int kRecP = kRecTpLo + kFrags * kFragBytes;     // P = tril(Q K^T o e^{G_i - G_j}), bf16
+// P = tril(Q K^T o e^{G_i - G_j}), bf16; its k-slots are permuted: fragment (row block, k step
+// ks), lane (row i, group g), slot e holds column 32 ks + 16 (e / 4) + 4 g + e % 4.  (T' uses the
+// plain order: slot e holds column 32 ks + 8 g + e.)
+constexpr int kRecP = kRecTpLo + kFrags * kFragBytes;
 constexpr int kRecEG = kRecP + kFrags * kFragBytes;       // e^{G_i}           fp32[64]
 constexpr int kRecED = kRecEG + kChunk * 4;               // e^{G_last - G_i}  fp32[64]
 constexpr int kRecBytes = kRecED + kChunk * 4;            // 18944

@@ -75,6 +75,13 @@ __device__ __forceinline__ int swz(int row, int col) {
 // which the LDS serves without bank conflicts (padded column-major rows conflict 4-way).
 __device__ __forceinline__ int vmaj(int j, int e) { return 16 * (16 * (e >> 3) + j) + 2 * (e & 7); }
 
+// U~ for the P U~ product, in the token order of P's k-slots (chunk_prep.hip writes P straight from
+// its accumulators): k-step ks, lane group g holds tokens 32 ks + 4 g .. + 3, then 32 ks + 16 + 4 g
+// .. + 3, stored as one 16-byte chunk at byte 16 (16 (4 ks + g) + j) for column j.
+__device__ __forceinline__ int pmaj(int j, int t) {
+  return 16 * (16 * (4 * (t >> 5) + ((t >> 2) & 3)) + j) + 8 * ((t >> 4) & 1) + 2 * (t & 3);
+}
+
 // State rows held by compute wave w: accumulator a, C-layout row i (0..15) is key
 // 8 (w + 8 a) + i for i < 8 and 8 (w + 8 a + 4) + i - 8 for i >= 8.  Taking the two 8-key
 // chunks of a K^T fragment 4 chunks apart keeps its transposing reads free of bank conflicts
@@ -368,17 +375,17 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
     split_pair(ed[2] * U[2], ed[3] * U[3], h1, l1);
     store_u32x2(Uh + vmaj(lj, 16 * w + 4 * lg), h0, h1);
     store_u32x2(Ul + vmaj(lj, 16 * w + 4 * lg), l0, l1);
-    store_u32x2(Uo + vmaj(lj, 16 * w + 4 * lg), pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
+    store_u32x2(Uo + pmaj(lj, 16 * w + 4 * lg), pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
   }
   __syncthreads();
 
   // o = e^G o (Q H) + P U~
   {
     O = mfma_bf16(lds_bf16x8(rs + kRecP + fb * kFragBytes + l * 16),
-                  lds_bf16x8(Uo + vmaj(lj, 8 * lg)), O);
+                  lds_bf16x8(Uo + pmaj(lj, 4 * lg)), O);
     if (w >= 2)
       O = mfma_bf16(lds_bf16x8(rs + kRecP + (fb + 1) * kFragBytes + l * 16),
-                    lds_bf16x8(Uo + vmaj(lj, 32 + 8 * lg)), O);
+                    lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)), O);
     // staging slot: rows 4 lg .. 4 lg + 3 of column lj at byte 8 (16 lg + lj) = 8 l, so the
     // write is lane-linear (the producers store it)
     store_u32x2(reinterpret_cast<unsigned short *>(oslot + 8 * l), pack_bf16x2(O[0], O[1]),
