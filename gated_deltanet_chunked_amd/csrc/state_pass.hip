@@ -22,7 +22,7 @@
 //   phase 2: U~ = T' R; U~ (decayed hi/lo and plain) to LDS                      -> b2
 //   phase 3: o = e^G o (Q H) + P U~ to an LDS staging slot; H update; bf16 H     -> b3
 // Data movement (four producer waves + four compute waves per workgroup, one of each per SIMD):
-//   * The producer waves do all of the global memory traffic, with global->LDS loads
+//   * The producer waves do all of the global loads, with global->LDS loads
 //     (global_load_lds_dwordx4: 1 KiB per instruction, no VGPRs).  The K, Q and V tiles are only
 //     read in phase 1, so their 2-deep ring slot is refilled with the tiles of chunk c + 2 right
 //     after b1 of chunk c; the record (T' hi/lo, P, decays), read until phase 3, has a 3-deep
@@ -47,7 +47,9 @@ constexpr int kHtBytes = kDvTile * kDim * 2;    // bf16 H exchange buffer
 constexpr int kXBytes = kDvTile * kChunk * 2;    // R / U~ exchange buffers
 constexpr int kComputeWaves = 4;
 constexpr int kProducerWaves = 4;     // one per SIMD, beside one compute wave
-constexpr int kPrefetchWave = kComputeWaves + kProducerWaves;
+constexpr int kOutputWaves = 4;       // one per SIMD, beside one compute wave
+constexpr int kOutputWave0 = kComputeWaves + kProducerWaves;
+constexpr int kPrefetchWave = kOutputWave0 + kOutputWaves;
 constexpr int kThreads = 64 * (kPrefetchWave + 1);
 constexpr int kPrefetchAhead = 6;     // chunks between the L2 warm-up of a chunk and its use
 // Tile ring slot: K tile | Q tile (64 x 128 bf16 each, swizzled) | V tile (64 x 16 bf16).
@@ -57,7 +59,7 @@ constexpr int kTQ = kTK + kChunk * kDim * 2;              // 16384
 constexpr int kTV = kTQ + kChunk * kDim * 2;              // 32768
 constexpr int kTileBytes = kTV + kChunk * kDvTile * 2;    // 34816
 constexpr int kRecStages = 3;                             // record ring slot: kRecBytes
-constexpr int kOBytes = 16 * kDvTile * 2;                 // one compute wave's 16 output rows
+constexpr int kOBytes = 16 * kDvTile * 2;                 // one row block's 16 output rows
 constexpr int kDmaTile = kChunk * kDim * 2 / 1024;        // 16 instructions of 1 KiB (K or Q)
 constexpr int kDmaRec = (kRecBytes + 1023) / 1024;        // 19 (the last one half full)
 constexpr int kDmaV = kChunk * kDvTile * 2 / 1024;        // 2
@@ -260,7 +262,7 @@ __device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, in
   return pf;
 }
 
-// Output rows 16 pw .. 16 pw + 15 of chunk c, left by compute wave pw in its staging slot (rows
+// Output rows 16 pw .. 16 pw + 15 of chunk c, left by output wave pw in its staging slot (rows
 // 4 g .. 4 g + 3 of column j at byte 8 (16 g + j)), to global memory.  One transposing read gives
 // lane i of lane group g row 4 g + i % 4, columns 4 (i / 4) .. + 3: lane r of the group names
 // column 4 (r % 4) + r / 4, rows 4 g .. 4 g + 3 (see lds_read_tr16).  ob points at column d0 of
@@ -277,20 +279,50 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
   }
 }
 
+// The output path o = e^G o (Q H) + P U~ for row block w of a chunk, on the output wave that
+// shares a SIMD with compute wave w.  It issues no global->LDS loads: a wave's LDS reads wait for
+// its own global->LDS loads still in flight, which would tie these reads to load latency.  out_qh
+// runs before b1: Q H needs the chunk's entry state, which the compute waves overwrite in phase 3,
+// and the Q tile, whose ring slot the producers refill after b1.  out_stage runs after b2, once U~
+// is in LDS: it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg ..
+// + 3 of column lj at byte 8 l); they are read back transposed and stored at the start of the
+// next chunk (store_o).
+__device__ __forceinline__ f32x4 out_qh(const unsigned char *qt, const unsigned char *Ht, int w, int l) {
+  const int lj = l & 15, lg = l >> 4;
+  f32x4 O = zero4();
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    O = mfma_bf16(lds_bf16x8(qt + swz(16 * w + lj, 32 * ks + 8 * lg)),
+                  lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), O);
+  return O;
+}
+__device__ __forceinline__ void out_stage(f32x4 O, const unsigned char *rs, const unsigned char *Uo,
+                                          int w, int l, unsigned char *oslot) {
+  const int lj = l & 15, lg = l >> 4;
+  const f32x4 eg = *reinterpret_cast<const f32x4 *>(rs + kRecEG + (16 * w + 4 * lg) * 4);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) O[rr] *= eg[rr];
+  const int fb = w < 2 ? w : 2 * w - 2;
+  O = mfma_bf16(lds_bf16x8(rs + kRecP + fb * kFragBytes + l * 16), lds_bf16x8(Uo + pmaj(lj, 4 * lg)), O);
+  if (w >= 2)
+    O = mfma_bf16(lds_bf16x8(rs + kRecP + (fb + 1) * kFragBytes + l * 16),
+                  lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)), O);
+  store_u32x2(oslot + 8 * l, pack_bf16x2(O[0], O[1]), pack_bf16x2(O[2], O[3]));
+}
+
 // One chunk on the compute waves.  Rows past the sequence end hold clamped data; they need no
 // masking because T' has zero rows and columns there (beta = 0), so U~ is zero on them, and
 // their output rows are never stored.  The chunk's K, Q and V tiles are in tile ring slot TS,
 // its record in record ring slot RS (compile-time, so that the slot offsets fold into the LDS
-// instructions); oslot is this wave's output staging slot.
+// instructions).  The output path runs on the output waves (out_qh, out_stage).
 template <int TS, int RS>
 __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const unsigned char *recs,
                                            int w, int l, f32x4 (&H)[2], unsigned char *Ht,
                                            unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
-                                           unsigned char *Ul, unsigned char *Uo,
-                                           unsigned char *oslot) {
+                                           unsigned char *Ul, unsigned char *Uo) {
   const int lj = l & 15, lg = l >> 4;
   const unsigned char *ts = tiles + TS * kTileBytes, *rs = recs + RS * kRecBytes;
-  const unsigned char *kt = ts + kTK, *qt = ts + kTQ;
+  const unsigned char *kt = ts + kTK;
 
   // K^T fragments for the state update, read transposed from the K tile: fragment (accumulator
   // a, token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][state_key(w, a, lj)].
@@ -310,16 +342,16 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
       kc[a][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
-  // X = K H and Q H (contraction over the 128 keys; B operand = bf16 H from LDS)
-  f32x4 X = zero4(), O = zero4();
+  // X = K H (contraction over the 128 keys; B operand = bf16 H from LDS), in two chains
+  f32x4 X = zero4(), X2 = zero4();
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 hb = lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg));
-    const bf16x8 kx = lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 8 * lg));
-    const bf16x8 qx = lds_bf16x8(qt + swz(16 * w + lj, 32 * ks + 8 * lg));
-    X = mfma_bf16(kx, hb, X);
-    O = mfma_bf16(qx, hb, O);
+  for (int ks = 0; ks < 4; ks += 2) {
+    X = mfma_bf16(lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 8 * lg)),
+                  lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), X);
+    X2 = mfma_bf16(lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 32 + 8 * lg)),
+                   lds_bf16x8(Ht + vmaj(lj, 32 * ks + 32 + 8 * lg)), X2);
   }
+  X += X2;
   const f32x4 eg = *reinterpret_cast<const f32x4 *>(rs + kRecEG + (16 * w + 4 * lg) * 4);
   const f32x4 ed = *reinterpret_cast<const f32x4 *>(rs + kRecED + (16 * w + 4 * lg) * 4);
   const float egc = *reinterpret_cast<const float *>(rs + kRecEG + 63 * 4);
@@ -332,14 +364,11 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
     for (int rr = 0; rr < 4; ++rr) vv[rr] = bits_to_float((unsigned short)v4[rr]);
   }
 
-  // R = V - e^G o X (hi/lo to LDS, value-major); O <- e^G o O
+  // R = V - e^G o X (hi/lo to LDS, value-major)
   {
     float R[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      R[rr] = vv[rr] - eg[rr] * X[rr];
-      O[rr] *= eg[rr];
-    }
+    for (int rr = 0; rr < 4; ++rr) R[rr] = vv[rr] - eg[rr] * X[rr];
     uint32_t h0, l0, h1, l1;
     split_pair(R[0], R[1], h0, l0);
     split_pair(R[2], R[3], h1, l1);
@@ -378,19 +407,6 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
     store_u32x2(Uo + pmaj(lj, 16 * w + 4 * lg), pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
   }
   __syncthreads();
-
-  // o = e^G o (Q H) + P U~
-  {
-    O = mfma_bf16(lds_bf16x8(rs + kRecP + fb * kFragBytes + l * 16),
-                  lds_bf16x8(Uo + pmaj(lj, 4 * lg)), O);
-    if (w >= 2)
-      O = mfma_bf16(lds_bf16x8(rs + kRecP + (fb + 1) * kFragBytes + l * 16),
-                    lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)), O);
-    // staging slot: rows 4 lg .. 4 lg + 3 of column lj at byte 8 (16 lg + lj) = 8 l, so the
-    // write is lane-linear (the producers store it)
-    store_u32x2(reinterpret_cast<unsigned short *>(oslot + 8 * l), pack_bf16x2(O[0], O[1]),
-                pack_bf16x2(O[2], O[3]));
-  }
 
   // H = e^{G_last} H + K^T (e^{G_last - G} o U~)  (decayed U~ hi + lo)
 #pragma unroll
@@ -477,6 +493,30 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     return;
   }
 
+  if (w >= kOutputWave0) {
+    // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  Q H
+    // is taken before b1 (the Q tile's slot is refilled after b1, H is rewritten in phase 3), P U~
+    // after b2 (U~ is complete); the rows are staged and stored at the start of the next chunk.
+    const int ow = w - kOutputWave0;
+    if (nc > 0) {
+      unsigned char *ob = reinterpret_cast<unsigned char *>(o + (size_t)h * kDim + d0);
+      unsigned char *oslot = ostage + ow * kOBytes;
+      const uint32_t ooff = (uint32_t)(16 * ow + 4 * (l >> 4) + (l & 3)) * (uint32_t)(Hv * kDim * 2) +
+                            8 * ((l & 15) >> 2);
+      __syncthreads();
+      for (int c = 0; c < nc; ++c) {
+        if (c > 0) store_o(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+        const f32x4 O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
+        __syncthreads();  // b1
+        __syncthreads();  // b2
+        out_stage(O, recs + (c % kRecStages) * kRecBytes, Uo, ow, l, oslot);
+        __syncthreads();  // b3
+      }
+      store_o(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+    }
+    return;
+  }
+
   if (w >= kComputeWaves) {
     // Producer waves.  Barriers: one before the loop, three per chunk, as the compute waves.
     const int pw = w - kComputeWaves;
@@ -486,16 +526,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       const unsigned char *kb = reinterpret_cast<const unsigned char *>(k + (size_t)hk * kDim);
       const unsigned char *qb = reinterpret_cast<const unsigned char *>(q + (size_t)hk * kDim);
       const unsigned char *vb = reinterpret_cast<const unsigned char *>(v + (size_t)h * kDim);
-      unsigned char *ob = reinterpret_cast<unsigned char *>(o + (size_t)h * kDim + d0);
-      const unsigned char *oslot = ostage + pw * kOBytes;
       ProducerLanes pl;
       pl.row0 = 4 * pw + (l >> 4);
       pl.lc = (l & 15) ^ (pl.row0 & 15);
       pl.tile = (uint32_t)pl.row0 * (uint32_t)(Hk * kDim * 2) + 16 * pl.lc;
       pl.v = (uint32_t)(l >> 1) * (uint32_t)(Hv * kDim * 2) + 2 * (d0 + 8 * (l & 1));
       pl.rec = 16 * l;
-      const uint32_t ooff = (uint32_t)(16 * pw + 4 * (l >> 4) + (l & 3)) * (uint32_t)(Hv * kDim * 2) +
-                            8 * ((l & 15) >> 2);
       const int c1 = min(1, nc - 1);
       dma_tiles(0, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl, tiles_lds);
       dma_rec<0>(slot0, h, Hv, pw, l, rec, pl, recs_lds);
@@ -512,7 +548,6 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         // before the last barrier; its tile slot c % 2 holds chunk c's tiles, done after b1.
         const int cn = min(c + 2, nc - 1);
         const unsigned rslot = recs_lds + ((c + 2) % kRecStages) * kRecBytes;
-        if (c > 0) store_o(c - 1, tb, te, Hv, pw, l, oslot, ob, ooff);
         dma_rec<0>(slot0 + cn, h, Hv, pw, l, rec, pl, rslot);
         __syncthreads();  // b1
         dma_tiles(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl,
@@ -524,7 +559,6 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         if (pw != 3) wait_vmcnt<kChunkCount(0)>(); else wait_vmcnt<kChunkCount(3)>();
         __syncthreads();  // b3
       }
-      store_o(nc - 1, tb, te, Hv, pw, l, oslot, ob, ooff);
     }
     wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
     return;
@@ -547,8 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
                   pack_bf16x2(H[a][2], H[a][3]));
     __syncthreads();
     // six chunks per trip, so that every chunk's ring slots (c % 2, c % 3) are compile-time
-    unsigned char *oslot = ostage + w * kOBytes;
-#define GDN_STEP(ts, rs) chunk_step<ts, rs>(tiles, recs, w, l, H, Ht, Rh, Rl, Uh, Ul, Uo, oslot)
+#define GDN_STEP(ts, rs) chunk_step<ts, rs>(tiles, recs, w, l, H, Ht, Rh, Rl, Uh, Ul, Uo)
     for (int c = 0; c < nc; c += 6) {
       GDN_STEP(0, 0);
       if (c + 1 == nc) break;
