@@ -109,19 +109,26 @@ static void recur_one(int64_t t_begin, int64_t t_end, int32_t Hk, int32_t Hv, in
 }
 
 /*
- * Gated delta rule over a packed batch.
+ * Gated delta rule over a packed batch, with the initial states drawn from a pool by index.
  *   q, k  : [T, Hk, dk]     v : [T, Hv, dv]     g, beta : [T, Hv]
  *   cu    : [N+1], cu[0] = 0, non-decreasing, cu[N] = T
- *   h0    : [N, Hv, dk, dv] or NULL;  hT : [N, Hv, dk, dv] or NULL
- *   o     : [T, Hv, dv]
+ *   h0    : [num_h0, Hv, dk, dv] or NULL (zero states)
+ *   h0_index : [N] or NULL.  Sequence n starts from h0[h0_index[n]] when that index lies in
+ *           [0, num_h0), and from a zero state otherwise.  NULL means sequence n starts from
+ *           h0[n] (then num_h0 must be N).  One prefix's final state handed to several
+ *           candidates is this with repeated indices ("open-jev-fast" README, "Phase 2" item 2;
+ *           PR #186, "Review scope and map").
+ *   hT    : [N, Hv, dk, dv] or NULL;  o : [T, Hv, dv]
  * Returns 0, or -1 on bad arguments.
  */
-int oracle_gdn_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
-                   const double *q, const double *k, const double *v, const double *g,
-                   const double *beta, const int64_t *cu, const double *h0, double *o,
-                   double *hT, int32_t nthreads) {
+int oracle_gdn_fwd_indexed(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                           const double *q, const double *k, const double *v, const double *g,
+                           const double *beta, const int64_t *cu, const double *h0,
+                           int32_t num_h0, const int64_t *h0_index, double *o, double *hT,
+                           int32_t nthreads) {
   if (N < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || dk < 1 || dv < 1 || T < 0) return -1;
   if (cu[0] != 0 || cu[N] != T) return -1;
+  if (!h0_index && h0 && num_h0 != N) return -1;
   for (int32_t n = 0; n < N; ++n)
     if (cu[n + 1] < cu[n]) return -1;
   const int64_t pairs = (int64_t)N * Hv;
@@ -145,7 +152,8 @@ int oracle_gdn_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int
 #endif
       for (int64_t p = 0; p < pairs; ++p) {
         const int32_t n = (int32_t)(p / Hv), h = (int32_t)(p % Hv);
-        const double *h0_nh = h0 ? h0 + ((int64_t)n * Hv + h) * state : NULL;
+        const int64_t r = h0_index ? h0_index[n] : n;
+        const double *h0_nh = (h0 && r >= 0 && r < num_h0) ? h0 + (r * Hv + h) * state : NULL;
         double *hT_nh = hT ? hT + ((int64_t)n * Hv + h) * state : NULL;
         recur_one(cu[n], cu[n + 1], Hk, Hv, dk, dv, h, q, k, v, g, beta, h0_nh, o, hT_nh, S,
                   u);
@@ -156,6 +164,15 @@ int oracle_gdn_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int
   }
   (void)nthreads;
   return bad ? -2 : 0;
+}
+
+/* The same with h0 : [N, Hv, dk, dv] or NULL, sequence n starting from h0[n]. */
+int oracle_gdn_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                   const double *q, const double *k, const double *v, const double *g,
+                   const double *beta, const int64_t *cu, const double *h0, double *o,
+                   double *hT, int32_t nthreads) {
+  return oracle_gdn_fwd_indexed(T, N, Hk, Hv, dk, dv, q, k, v, g, beta, cu, h0, N, NULL, o, hT,
+                                nthreads);
 }
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -178,32 +195,62 @@ void oracle_round_bf16_array(const double *x, double *out, int64_t n) {
 }
 
 /*
- * Causal depthwise conv1d + SiLU over a packed batch (the first part of the
- * GDN input prep).  x : [T, C];  w : [C, taps], tap taps-1 multiplies the
- * current token; the window never reaches across a sequence start.
- * out : [T, C].
+ * Causal depthwise conv1d + SiLU over a packed batch (the first part of the GDN input prep),
+ * with a carried input window per sequence.
+ *   x : [T, C];  w : [C, taps], tap taps-1 multiplies the current token.
+ *   win_in : [num_states, taps-1, C] or NULL -- the last taps-1 conv inputs before a sequence
+ *            start, oldest first.  Sequence n reads window win_in[state_index[n]] when that index
+ *            lies in [0, num_states), else a window of zeros; a NULL state_index means window n
+ *            (then num_states must be N).  A NULL win_in means zeros before every sequence start.
+ *   out : [T, C].
+ *   win_out : [N, taps-1, C] or NULL -- the last taps-1 inputs of sequence n's stream (its
+ *            window followed by its tokens), oldest first: the window the next call continues
+ *            from.  (The prefix handing its conv window and recurrent state on to a candidate:
+ *            "open-jev-fast" README, "Phase 2" item 2.)
+ * The window never reaches across a sequence start into another sequence's tokens.
  */
-int oracle_conv_silu(int64_t T, int32_t N, int32_t C, int32_t taps, const double *x,
-                     const double *w, const int64_t *cu, double *out, int32_t nthreads) {
-  if (cu[0] != 0 || cu[N] != T) return -1;
+int oracle_conv_silu_cont(int64_t T, int32_t N, int32_t C, int32_t taps, const double *x,
+                          const double *w, const int64_t *cu, const double *win_in,
+                          int32_t num_states, const int64_t *state_index, double *out,
+                          double *win_out, int32_t nthreads) {
+  if (cu[0] != 0 || cu[N] != T || taps < 1) return -1;
+  if (!state_index && win_in && num_states != N) return -1;
+  const int64_t wrows = (int64_t)(taps - 1) * C;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(static)
 #endif
   for (int32_t ch = 0; ch < C; ++ch) {
     for (int32_t n = 0; n < N; ++n) {
+      const int64_t r = state_index ? state_index[n] : n;
+      const double *win = (win_in && r >= 0 && r < num_states) ? win_in + r * wrows : NULL;
       for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
         double c = 0.0;
         for (int32_t j = 0; j < taps; ++j) {
           const int64_t src = t - (taps - 1) + j;
           if (src >= cu[n]) c += w[(int64_t)ch * taps + j] * x[src * C + ch];
+          else if (win) c += w[(int64_t)ch * taps + j] * win[(src - cu[n] + taps - 1) * C + ch];
         }
         out[t * C + ch] = c * sigmoid(c);
       }
+      if (win_out)
+        for (int32_t j = 0; j < taps - 1; ++j) {
+          const int64_t p = cu[n + 1] - (taps - 1) + j;  /* stream position, >= cu[n] - (taps-1) */
+          double val = 0.0;
+          if (p >= cu[n]) val = x[p * C + ch];
+          else if (win) val = win[(p - cu[n] + taps - 1) * C + ch];
+          win_out[(int64_t)n * wrows + (int64_t)j * C + ch] = val;
+        }
     }
   }
   (void)nthreads;
   return 0;
+}
+
+/* The same with zeros before every sequence start and no window out. */
+int oracle_conv_silu(int64_t T, int32_t N, int32_t C, int32_t taps, const double *x,
+                     const double *w, const int64_t *cu, double *out, int32_t nthreads) {
+  return oracle_conv_silu_cont(T, N, C, taps, x, w, cu, NULL, N, NULL, out, NULL, nthreads);
 }
 
 /*
@@ -211,16 +258,21 @@ int oracle_conv_silu(int64_t T, int32_t N, int32_t C, int32_t taps, const double
  * inside each), L2 norm of q and k per head, the gated delta rule, then the
  * SiLU(z)-gated RMSNorm per (token, v-head) with a weight shared by all heads.
  *   qkv [T, 2*Hk*dk + Hv*dv], conv_w [2*Hk*dk + Hv*dv, taps], g/beta [T, Hv],
- *   z [T, Hv, dv], norm_w [dv], h0 [N, Hv, dk, dv] or NULL
- *   -> y [T, Hv, dv], hT [N, Hv, dk, dv] or NULL.
+ *   z [T, Hv, dv], norm_w [dv]
+ *   h0 [num_states, Hv, dk, dv] or NULL, conv_in [num_states, taps-1, 2*Hk*dk + Hv*dv] or NULL,
+ *   state_index [N] or NULL: sequence n continues from recurrent state and conv window
+ *   state_index[n] (zeros when that index is outside [0, num_states)); NULL means state n.
+ *   -> y [T, Hv, dv], hT [N, Hv, dk, dv] or NULL, conv_out [N, taps-1, C] or NULL.
  * Intermediates (q, k, v after prep; o) are fp64 throughout.
  */
-int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
-                     int32_t taps, double eps_l2, double eps_norm, int32_t bf16_points,
-                     const double *qkv,
-                     const double *conv_w, const double *g, const double *beta,
-                     const double *z, const double *norm_w, const int64_t *cu,
-                     const double *h0, double *y, double *hT, int32_t nthreads) {
+int oracle_mixer_fwd_cont(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk,
+                          int32_t dv, int32_t taps, double eps_l2, double eps_norm,
+                          int32_t bf16_points, const double *qkv, const double *conv_w,
+                          const double *g, const double *beta, const double *z,
+                          const double *norm_w, const int64_t *cu, const double *h0,
+                          const double *conv_in, int32_t num_states,
+                          const int64_t *state_index, double *y, double *hT, double *conv_out,
+                          int32_t nthreads) {
   const int32_t Cq = Hk * dk, Cv = Hv * dv, C = 2 * Cq + Cv;
   const int64_t Tn = T > 0 ? T : 1;
   double *a = (double *)malloc(sizeof(double) * Tn * C);
@@ -230,7 +282,8 @@ int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, i
   double *o = (double *)malloc(sizeof(double) * Tn * Cv);
   int rc = -2;
   if (!a || !q || !k || !v || !o) goto done;
-  rc = oracle_conv_silu(T, N, C, taps, qkv, conv_w, cu, a, nthreads);
+  rc = oracle_conv_silu_cont(T, N, C, taps, qkv, conv_w, cu, conv_in, num_states, state_index, a,
+                             conv_out, nthreads);
   if (rc) goto done;
   for (int64_t t = 0; t < T; ++t) {
     const double *row = a + t * C;
@@ -257,7 +310,8 @@ int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, i
     }
     for (int64_t e = 0; e < T * Cv; ++e) v[e] = oracle_round_bf16(v[e]);
   }
-  rc = oracle_gdn_fwd(T, N, Hk, Hv, dk, dv, q, k, v, g, beta, cu, h0, o, hT, nthreads);
+  rc = oracle_gdn_fwd_indexed(T, N, Hk, Hv, dk, dv, q, k, v, g, beta, cu, h0, num_states,
+                              state_index, o, hT, nthreads);
   if (rc) goto done;
   if (bf16_points)
     for (int64_t e = 0; e < T * Cv; ++e) o[e] = oracle_round_bf16(o[e]);
@@ -279,4 +333,16 @@ done:
   free(v);
   free(o);
   return rc;
+}
+
+/* The mixer with zero conv history and h0[n] (or zeros) for sequence n, no window out. */
+int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                     int32_t taps, double eps_l2, double eps_norm, int32_t bf16_points,
+                     const double *qkv, const double *conv_w, const double *g,
+                     const double *beta, const double *z, const double *norm_w,
+                     const int64_t *cu, const double *h0, double *y, double *hT,
+                     int32_t nthreads) {
+  return oracle_mixer_fwd_cont(T, N, Hk, Hv, dk, dv, taps, eps_l2, eps_norm, bf16_points, qkv,
+                               conv_w, g, beta, z, norm_w, cu, h0, NULL, N, NULL, y, hT, NULL,
+                               nthreads);
 }

@@ -337,3 +337,129 @@ def pin_round_bf16_matches_torch(conv, mixer, fwd, lib=None):
 
 
 MIXER_PINS = [pin_conv_torch, pin_conv_delta_taps, pin_mixer_torch, pin_round_bf16_matches_torch]
+
+
+# ------------------------------------------------------------------------------------------
+# P-10 (continuation): initial states drawn from a pool by index, and the conv input window
+# carried from one call to the next (a prefix hands its conv window and recurrent state to each
+# candidate).  Each takes ``api`` with the callables fwd, fwd_idx, conv_cont, mixer_cont
+# (signatures of oracle.gdn_fwd, gdn_fwd_indexed, conv_silu_cont, mixer_fwd_cont).
+# ------------------------------------------------------------------------------------------
+def pin_fanout_brute(api, d=3, seed=41):
+    """Exact rational brute force per sequence with S_0 = pool[index] (zero when out of range)."""
+    from oracle import brute
+    rng = np.random.default_rng(seed)
+    R = lambda: Fraction(int(rng.integers(-8, 9)), 8)
+    lengths = [3, 2, 0, 4, 2]
+    index = [1, 1, 0, -1, 5]  # repeated, an empty sequence, negative and past-the-end indices
+    pool = [[[R() for _ in range(d)] for _ in range(d)] for _ in range(2)]  # value-major S_0
+    T = sum(lengths)
+    alpha = [Fraction(int(rng.integers(1, 9)), 8) for _ in range(T)]
+    beta = [Fraction(int(rng.integers(0, 9)), 8) for _ in range(T)]
+    q = [[R() for _ in range(d)] for _ in range(T)]
+    k = [[R() for _ in range(d)] for _ in range(T)]
+    v = [[R() for _ in range(d)] for _ in range(T)]
+    f = lambda m: np.array([[float(x) for x in r] for r in m])
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    h0 = np.stack([f(S).T for S in pool])[:, None]  # [2, 1, d, d] key-major
+    o, hT = api.fwd_idx(f(q)[:, None], f(k)[:, None], f(v)[:, None],
+                        np.log(np.array([float(a) for a in alpha]))[:, None],
+                        np.array([float(b) for b in beta])[:, None], cu, h0, index)
+    zero = [[Fraction(0)] * d for _ in range(d)]
+    for n, L in enumerate(lengths):
+        S0 = pool[index[n]] if 0 <= index[n] < 2 else zero
+        sl = slice(cu[n], cu[n + 1])
+        if L == 0:  # an empty sequence hands its initial state through
+            assert np.array_equal(hT[n, 0], f(S0).T), "fan-out hT (empty sequence)"
+            continue
+        outs, ST = brute.run(alpha[sl], beta[sl], q[sl], k[sl], v[sl], S0)
+        assert np.allclose(o[sl, 0], f(outs), rtol=1e-12, atol=1e-13), "fan-out o"
+        assert np.allclose(hT[n, 0], f(ST).T, rtol=1e-12, atol=1e-13), "fan-out hT"
+
+
+def pin_fanout_equals_gathered(api):
+    """Indexing the pool equals handing each sequence an explicit copy (bitwise)."""
+    rng = np.random.default_rng(42)
+    q, k, v, g, beta, cu, _ = _rand_case(rng, 0, 2, 4, 8, lengths=[9, 70, 0, 5, 33], h0=False)
+    pool = rng.standard_normal((3, 4, 8, 8)) * 0.3
+    index = np.array([2, 0, 2, 3, 2])  # index 3 is outside the pool: zero state
+    o, hT = api.fwd_idx(q, k, v, g, beta, cu, pool, index)
+    gathered = np.stack([pool[i] if 0 <= i < 3 else np.zeros((4, 8, 8)) for i in index])
+    o2, h2 = api.fwd(q, k, v, g, beta, cu, gathered)
+    assert np.array_equal(o, o2) and np.array_equal(hT, h2), "fan-out vs copies"
+
+
+def pin_conv_window_numpy(api):
+    """Conv over (window ++ tokens) against numpy's correlate; the window out is the stream's last
+    taps-1 entries -- for sequences shorter than the window too."""
+    rng = np.random.default_rng(43)
+    C, taps = 6, 4
+    lengths = [0, 1, 2, 3, 9]
+    index = np.array([2, 0, -1, 0, 7])
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    x = rng.standard_normal((cu[-1], C))
+    w = 0.5 * rng.standard_normal((C, taps))
+    pool = rng.standard_normal((3, taps - 1, C))
+    out, wout = api.conv_cont(x, w, cu, pool, index)
+    for n in range(len(lengths)):
+        win = pool[index[n]] if 0 <= index[n] < 3 else np.zeros((taps - 1, C))
+        stream = np.concatenate([win, x[cu[n]:cu[n + 1]]])
+        for ch in range(C if lengths[n] else 0):
+            c = np.correlate(stream[:, ch], w[ch], mode="valid")
+            assert np.allclose(out[cu[n]:cu[n + 1], ch], c / (1 + np.exp(-c)), rtol=1e-12, atol=1e-13), "conv window"
+        assert np.array_equal(wout[n], stream[-(taps - 1):]), "window out"
+
+
+def _mixer_case(rng, lengths, Hk=2, Hv=4, d=8):
+    T = sum(lengths)
+    C = 2 * Hk * d + Hv * d
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return dict(qkv=rng.standard_normal((T, C)), conv_w=0.5 * rng.standard_normal((C, 4)),
+                g=-np.log1p(np.exp(-(3 + rng.standard_normal((T, Hv))))),
+                beta=1 / (1 + np.exp(-rng.standard_normal((T, Hv)))), z=rng.standard_normal((T, Hv, d)),
+                norm_w=1 + 0.1 * rng.standard_normal(d), cu=cu, Hk=Hk, Hv=Hv, d=d)
+
+
+def _mix(api, m, sl_tok, cu, h0, conv_in, index, points):
+    return api.mixer_cont(m["qkv"][sl_tok], m["conv_w"], m["g"][sl_tok], m["beta"][sl_tok], m["z"][sl_tok],
+                          m["norm_w"], cu, h0, conv_in, index, Hk=m["Hk"], Hv=m["Hv"], dk=m["d"], dv=m["d"],
+                          bf16_points=points)
+
+
+def pin_mixer_split_continuation(api):
+    """Two sequences, each cut at s: running the tails from the heads' states and windows equals
+    one run of the whole sequences (bitwise, with and without the bf16 points)."""
+    rng = np.random.default_rng(44)
+    m = _mixer_case(rng, [13, 21])
+    L = [13, 21]
+    h0 = 0.1 * rng.standard_normal((2, m["Hv"], m["d"], m["d"]))
+    for points in (False, True):
+        y, hT, wout = _mix(api, m, slice(None), m["cu"], h0, None, None, points)
+        for s in (1, 2, 7):
+            head = np.concatenate([np.arange(s), 13 + np.arange(s)])
+            tail = np.concatenate([np.arange(s, 13), 13 + np.arange(s, 21)])
+            ya, ha, wa = _mix(api, m, head, [0, s, 2 * s], h0, None, None, points)
+            yb, hb, wb = _mix(api, m, tail, [0, 13 - s, 34 - 2 * s], ha, wa, None, points)
+            yy = np.zeros_like(y)
+            yy[head], yy[tail] = ya, yb
+            assert np.array_equal(yy, y), f"mixer continuation y (split {s})"
+            assert np.array_equal(hb, hT) and np.array_equal(wb, wout), f"mixer continuation state (split {s})"
+
+
+def pin_mixer_fanout(api):
+    """Indexed pools of states and windows equal explicitly gathered copies (bitwise)."""
+    rng = np.random.default_rng(45)
+    m = _mixer_case(rng, [5, 0, 17, 2])
+    C = m["qkv"].shape[1]
+    h0 = 0.1 * rng.standard_normal((2, m["Hv"], m["d"], m["d"]))
+    win = rng.standard_normal((2, 3, C))
+    index = np.array([1, 1, -1, 0])
+    y, hT, wout = _mix(api, m, slice(None), m["cu"], h0, win, index, True)
+    gh = np.stack([h0[i] if 0 <= i < 2 else np.zeros_like(h0[0]) for i in index])
+    gw = np.stack([win[i] if 0 <= i < 2 else np.zeros_like(win[0]) for i in index])
+    y2, h2, w2 = _mix(api, m, slice(None), m["cu"], gh, gw, None, True)
+    assert np.array_equal(y, y2) and np.array_equal(hT, h2) and np.array_equal(wout, w2), "mixer fan-out"
+
+
+CONT_PINS = [pin_fanout_brute, pin_fanout_equals_gathered, pin_conv_window_numpy, pin_mixer_split_continuation,
+             pin_mixer_fanout]

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from tests import oracle_pins as P
+from tests.test_oracle_pins import oracle_api
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
 
@@ -49,12 +50,20 @@ MUTANTS = {
     "gqa_modulo_map": [("const int32_t hk = h / group;", "const int32_t hk = h % Hk;")],
     "sequence_start_ignored": [("recur_one(cu[n], cu[n + 1],", "recur_one(n ? cu[n] - 1 : 0, cu[n + 1],")],
     "conv_crosses_sequences": [("if (src >= cu[n]) c +=", "if (src >= 0) c +=")],
-    "conv_tap_reversed": [("c += w[(int64_t)ch * taps + j] *", "c += w[(int64_t)ch * taps + (taps - 1 - j)] *")],
+    "conv_tap_reversed": [("c += w[(int64_t)ch * taps + j] * x[src", "c += w[(int64_t)ch * taps + (taps - 1 - j)] * x[src")],
     "rmsnorm_sum_not_mean": [("sqrt(ms / dv + eps_norm)", "sqrt(ms + eps_norm)")],
     "gate_without_silu": [("norm_w[j] * zs[j] * sigmoid(zs[j])", "norm_w[j] * sigmoid(zs[j])")],
     "l2norm_missing_on_k": [("k[(t * Hk + hh) * dk + j] = ks[j] * rk;", "k[(t * Hk + hh) * dk + j] = ks[j];")],
     "bf16_ties_away": [("(diff == 0.5 && fmod(r, 2.0) != 0.0)", "(diff == 0.5)")],
     "bf16_truncates": [("if (diff > 0.5 ||", "if (0 &&")],
+    "state_index_ignored": [("const int64_t r = h0_index ? h0_index[n] : n;", "const int64_t r = n;")],
+    "out_of_range_index_reads_row_0": [("(h0 && r >= 0 && r < num_h0) ? h0 + (r * Hv + h) * state",
+                                        "h0 ? h0 + ((r >= 0 && r < num_h0) ? r : 0) * Hv * state + h * state")],
+    "window_index_ignored": [("const int64_t r = state_index ? state_index[n] : n;", "const int64_t r = n;")],
+    "window_ignored": [("else if (win) c +=", "else if (0) c +=")],
+    "window_reversed": [("win[(src - cu[n] + taps - 1) * C + ch];", "win[(cu[n] - 1 - src) * C + ch];")],
+    "window_out_shifted": [("const int64_t p = cu[n + 1] - (taps - 1) + j;", "const int64_t p = cu[n + 1] - taps + j;")],
+    "window_out_drops_carried": [("else if (win) val =", "else if (0) val =")],
     "bf16_point_on_o_missing": [("for (int64_t e = 0; e < T * Cv; ++e) o[e] = oracle_round_bf16(o[e]);", ";")],
 }
 
@@ -89,6 +98,11 @@ def test_mutant_is_caught(tmp_path, name):
             pin(conv, mixer, fwd)
         except (AssertionError, RuntimeError, ValueError):
             caught.append(pin.__name__)
+    for pin in P.CONT_PINS:
+        try:
+            pin(oracle_api(lib))
+        except (AssertionError, RuntimeError, ValueError):
+            caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
 
 
@@ -99,3 +113,5 @@ def test_unmutated_copy_passes(tmp_path):
         pin(fwd)
     for pin in P.MIXER_PINS:
         pin(functools.partial(oracle.conv_silu, lib=lib), functools.partial(oracle.mixer_fwd, lib=lib), fwd)
+    for pin in P.CONT_PINS:
+        pin(oracle_api(lib))

@@ -52,3 +52,36 @@ def test_rejects_bad_cu_seqlens():
 @pytest.mark.parametrize("pin", P.MIXER_PINS, ids=lambda f: f.__name__)
 def test_mixer_pin(pin):
     pin(oracle.conv_silu, oracle.mixer_fwd, oracle.gdn_fwd)
+
+
+# ---------------------------------------------------------------------------------------------
+# Continuation: states by index, carried conv windows
+# ---------------------------------------------------------------------------------------------
+def oracle_api(lib=None):
+    import functools
+    from types import SimpleNamespace
+    kw = {} if lib is None else {"lib": lib}
+    return SimpleNamespace(fwd=functools.partial(oracle.gdn_fwd, **kw),
+                           fwd_idx=functools.partial(oracle.gdn_fwd_indexed, **kw),
+                           conv_cont=functools.partial(oracle.conv_silu_cont, **kw),
+                           mixer_cont=functools.partial(oracle.mixer_fwd_cont, **kw))
+
+
+@pytest.mark.parametrize("pin", P.CONT_PINS, ids=lambda f: f.__name__)
+def test_continuation_pin(pin):
+    pin(oracle_api())
+
+
+def test_plain_entry_points_equal_the_general_ones():
+    # gdn_fwd / mixer_fwd are the indexed / continued forms with identity map and no window
+    rng = np.random.default_rng(46)
+    q, k, v, g, beta, cu, h0 = P._rand_case(rng, 0, 2, 4, 8, lengths=[10, 3])
+    a = oracle.gdn_fwd(q, k, v, g, beta, cu, h0)
+    b = oracle.gdn_fwd_indexed(q, k, v, g, beta, cu, h0, [0, 1])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    m = P._mixer_case(rng, [6, 9])
+    y, hT = oracle.mixer_fwd(m["qkv"], m["conv_w"], m["g"], m["beta"], m["z"], m["norm_w"], m["cu"],
+                             Hk=2, Hv=4, dk=8, dv=8)
+    y2, h2, _ = oracle.mixer_fwd_cont(m["qkv"], m["conv_w"], m["g"], m["beta"], m["z"], m["norm_w"], m["cu"],
+                                      Hk=2, Hv=4, dk=8, dv=8)
+    assert np.array_equal(y, y2) and np.array_equal(hT, h2)
