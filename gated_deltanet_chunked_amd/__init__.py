@@ -8,9 +8,12 @@ Entry points (same names as the C ABI):
     gdn_abi_version(), gdn_status_string(code), gdn_last_hip_error()
     gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
     gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, hT)
+    gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, ...) -> (o, hT)
     gdn_chunk_prep / gdn_state_pass: the two stages of gdn_chunk_fwd (see ChunkPlan)
     gdn_mixer_fwd_workspace_size(T, N, Hk, Hv)
     gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, ...) -> (y, hT)
+    gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, ...)
+        -> (y, hT, conv_out)
 
 Layouts (row-major, contiguous): q, k bf16 [T, Hk, 128]; v bf16 [T, Hv, 128]; g, beta fp32
 [T, Hv]; cu_seqlens int32 [N+1]; h0, hT fp32 [N, Hv, 128, 128] key-major (H = S^T); o bf16
@@ -32,8 +35,8 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED = 0, 1, 2, 3
 GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_ALIAS, GDN_ERR_HIP = 4, 5, 6, 7
 
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_last_hip_error",
-                    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_prep", "gdn_state_pass",
-                    "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd")
+                    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_indexed", "gdn_chunk_prep",
+                    "gdn_state_pass", "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd", "gdn_mixer_fwd_cont")
 
 
 class ChunkDesc(ctypes.Structure):
@@ -75,6 +78,8 @@ def lib():
         L.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc)]
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 10
+        L.gdn_chunk_fwd_indexed.restype = ctypes.c_int
+        L.gdn_chunk_fwd_indexed.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 7 + [ctypes.c_int32] + [P] * 4
         L.gdn_chunk_prep.restype = ctypes.c_int
         L.gdn_chunk_prep.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 6
         L.gdn_state_pass.restype = ctypes.c_int
@@ -83,6 +88,8 @@ def lib():
         L.gdn_mixer_fwd_workspace_size.argtypes = [ctypes.POINTER(MixerDesc)]
         L.gdn_mixer_fwd.restype = ctypes.c_int
         L.gdn_mixer_fwd.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11
+        L.gdn_mixer_fwd_cont.restype = ctypes.c_int
+        L.gdn_mixer_fwd_cont.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 9 + [ctypes.c_int32] + [P] * 5
         _lib_handle = L
     return _lib_handle
 
@@ -142,13 +149,7 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, want_state=True,
-                  workspace=None, stream=None, cu_seqlens_host=None):
-    """Chunked gated-delta-rule forward.  Returns (o, hT) (hT is None if not wanted).
-
-    ``cu_seqlens_host`` (a CPU copy) avoids the device sync of checking ``cu_seqlens``.
-    ``workspace`` (uint8 CUDA tensor) may be passed to avoid an allocation per call.
-    """
+def _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace, cu_seqlens_host):
     dev = q.device
     T, Hk = int(q.shape[0]), int(q.shape[1])
     Hv = int(v.shape[1])
@@ -159,8 +160,6 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, wan
     _check(beta, "beta", torch.float32, (T, Hv), dev)
     N = _check_cu(cu_seqlens, T, cu_seqlens_host)
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
-    if h0 is not None:
-        _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
     if o is None:
         o = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
     _check(o, "o", torch.bfloat16, (T, Hv, D), dev)
@@ -173,11 +172,44 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, wan
         raise GdnError(GDN_ERR_SHAPE, "gdn_chunk_fwd_workspace_size")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    d = _desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel())
+    return T, N, Hk, Hv, o, hT, _desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel())
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, want_state=True,
+                  workspace=None, stream=None, cu_seqlens_host=None):
+    """Chunked gated-delta-rule forward.  Returns (o, hT) (hT is None if not wanted).
+
+    ``cu_seqlens_host`` (a CPU copy) avoids the device sync of checking ``cu_seqlens``.
+    ``workspace`` (uint8 CUDA tensor) may be passed to avoid an allocation per call.
+    """
+    T, N, Hk, Hv, o, hT, d = _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace,
+                                       cu_seqlens_host)
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (N, Hv, D, D), q.device)
     rc = lib().gdn_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                              _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd")
+    return o, hT
+
+
+def gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, *, o=None, hT=None, want_state=True,
+                          workspace=None, stream=None, cu_seqlens_host=None):
+    """gdn_chunk_fwd with sequence n starting from ``h0[h0_index[n]]`` of a pool of initial states
+    (h0: fp32 [num_h0, Hv, 128, 128]; h0_index: int32 [N] on the device; an index outside
+    [0, num_h0) means a zero state).  One prefix state fans out to many candidates without copies.
+    hT may not overlap h0.  Returns (o, hT)."""
+    T, N, Hk, Hv, o, hT, d = _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace,
+                                       cu_seqlens_host)
+    if h0.dim() != 4 or h0.shape[0] < 1:
+        raise ValueError("h0 must be [num_h0, Hv, 128, 128] with num_h0 >= 1")
+    _check(h0, "h0", torch.float32, (int(h0.shape[0]), Hv, D, D), q.device)
+    _check(h0_index, "h0_index", torch.int32, (N,), q.device)
+    rc = lib().gdn_chunk_fwd_indexed(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(cu_seqlens), _ptr(h0), int(h0.shape[0]), _ptr(h0_index), _ptr(o),
+                                     _ptr(hT), _stream(stream))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_indexed")
     return o, hT
 
 
@@ -233,6 +265,25 @@ class ChunkPlan:
 def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16, Hv=32, y=None, hT=None,
                   want_state=True, norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
     """GDN mixer forward (conv + SiLU + L2 norm, the chunked rule, gated RMSNorm).  Returns (y, hT)."""
+    y, hT, _ = _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, None, None, False, Hk, Hv, y, hT, None,
+                      want_state, False, norm_eps, workspace, stream, cu_seqlens_host)
+    return y, hT
+
+
+def gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, conv_in=None, state_index=None, *,
+                       Hk=16, Hv=32, y=None, hT=None, conv_out=None, want_state=True, want_window=True,
+                       norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
+    """The mixer continuing from carried states: sequence n starts from recurrent state and conv
+    window ``state_index[n]`` (int32 [N] on the device; None = state n) of the pools h0 (fp32
+    [S, Hv, 128, 128]) and conv_in (bf16 [S, 3, C], the last 3 qkv rows before the sequence,
+    oldest first); either pool may be None (zeros).  Returns (y, hT, conv_out) with conv_out bf16
+    [N, 3, C], the window the next call continues from."""
+    return _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, True, Hk, Hv, y, hT,
+                  conv_out, want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host)
+
+
+def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, cont, Hk, Hv, y, hT, conv_out,
+           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host):
     dev = qkv.device
     T = int(qkv.shape[0])
     C = (2 * Hk + Hv) * D
@@ -244,8 +295,17 @@ def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16
     _check(norm_w, "norm_w", torch.bfloat16, (D,), dev)
     N = _check_cu(cu_seqlens, T, cu_seqlens_host)
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    S = N
+    if state_index is not None:
+        _check(state_index, "state_index", torch.int32, (N,), dev)
+        pools = [int(t.shape[0]) for t in (h0, conv_in) if t is not None]
+        if len(set(pools)) > 1:
+            raise ValueError("h0 and conv_in pools must have the same number of states")
+        S = pools[0] if pools else 1
     if h0 is not None:
-        _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
+        _check(h0, "h0", torch.float32, (S, Hv, D, D), dev)
+    if conv_in is not None:
+        _check(conv_in, "conv_in", torch.bfloat16, (S, 3, C), dev)
     if y is None:
         y = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
     _check(y, "y", torch.bfloat16, (T, Hv, D), dev)
@@ -253,14 +313,25 @@ def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16
         hT = torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
     if hT is not None:
         _check(hT, "hT", torch.float32, (N, Hv, D, D), dev)
+    if conv_out is None and cont and want_window:
+        conv_out = torch.empty((N, 3, C), dtype=torch.bfloat16, device=dev)
+    if conv_out is not None:
+        _check(conv_out, "conv_out", torch.bfloat16, (N, 3, C), dev)
     need = gdn_mixer_fwd_workspace_size(T, N, Hk, Hv, 4, norm_eps)
     if need == 0:
         raise GdnError(GDN_ERR_SHAPE, "gdn_mixer_fwd_workspace_size")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     m = MixerDesc(_desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), 4, float(norm_eps))
-    rc = lib().gdn_mixer_fwd(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
-                             _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream))
+    if cont:
+        rc = lib().gdn_mixer_fwd_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
+                                      _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(conv_in), S, _ptr(state_index),
+                                      _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream))
+        where = "gdn_mixer_fwd_cont"
+    else:
+        rc = lib().gdn_mixer_fwd(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
+                                 _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream))
+        where = "gdn_mixer_fwd"
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_mixer_fwd")
-    return y, hT
+        raise GdnError(rc, where)
+    return y, hT, conv_out

@@ -13,10 +13,14 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
                        void *rec, hipStream_t stream);
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
-                       const float *h0, void *o, float *hT, const void *rec, int N, int Hk, int Hv,
-                       hipStream_t stream);
+                       const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
+                       const void *rec, int N, int Hk, int Hv, hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
-                       int Hk, int Hv, void *q, void *k, void *v, hipStream_t stream);
+                       int Hk, int Hv, const void *conv_in, const int32_t *state_index,
+                       int num_states, void *q, void *k, void *v, hipStream_t stream);
+void launch_conv_window_out(const void *qkv, const int32_t *cu, int N, int C,
+                            const void *conv_in, const int32_t *state_index, int num_states,
+                            void *conv_out, hipStream_t stream);
 void launch_gated_rmsnorm(const void *o, const void *z, const void *norm_w, float eps, int64_t T,
                           int Hv, void *y, hipStream_t stream);
 }  // namespace gdn
@@ -40,6 +44,26 @@ bool overlap(Range a, Range b) {
 }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// GDN_ERR_ALIAS if two outputs overlap, or an output overlaps an input -- except an output that
+// is exactly an input named as its in-place partner (same address; same extent by construction).
+struct InPlace {
+  const void *out, *in;
+};
+template <size_t NO, size_t NI, size_t NP>
+int check_alias(const Range (&outs)[NO], const Range (&ins)[NI], const InPlace (&ok)[NP]) {
+  for (size_t a = 0; a < NO; ++a)
+    for (size_t b = a + 1; b < NO; ++b)
+      if (overlap(outs[a], outs[b])) return GDN_ERR_ALIAS;
+  for (const Range &o : outs)
+    for (const Range &i : ins) {
+      if (!overlap(o, i)) continue;
+      bool allowed = false;
+      for (const InPlace &e : ok) allowed |= e.out && o.p == i.p && e.out == o.p && e.in == i.p;
+      if (!allowed) return GDN_ERR_ALIAS;
+    }
+  return GDN_OK;
+}
 
 // Checks the shape part of a descriptor; fills derived sizes.
 struct Shape {
@@ -76,10 +100,18 @@ int record_hip(hipError_t e) {
 
 enum Stage { kPrep = 1, kPass = 2, kBoth = 3 };
 
+// Initial states: h0 is [rows, Hv, dk, dv]; sequence n reads row index[n] (zeros when outside
+// [0, rows)), or row n when index is NULL (then rows == N).
+struct StatePool {
+  const float *h0;
+  int rows;
+  const int32_t *index;
+};
+
 // Validates the arguments a chunk-path stage reads and writes (unused pointers are ignored).
 int check_chunk_args(const gdn_chunk_desc *d, Shape &s, Stage stage, const void *q, const void *k,
                      const void *v, const float *g, const float *beta, const int32_t *cu,
-                     const float *h0, const void *o, const float *hT) {
+                     StatePool &pool, const void *o, const float *hT) {
   int st = check_shape(d, s);
   if (st != GDN_OK) return st;
   const bool tok = s.T > 0;
@@ -88,35 +120,36 @@ int check_chunk_args(const gdn_chunk_desc *d, Shape &s, Stage stage, const void 
   if (tok && (!q || !k)) return GDN_ERR_NULL;
   if (tok && prep && (!g || !beta)) return GDN_ERR_NULL;
   if (tok && pass && (!v || !o)) return GDN_ERR_NULL;
+  if (pool.index && pool.rows < 1) return GDN_ERR_SHAPE;
+  if (!pool.index) pool.rows = s.N;
   const size_t need = s.rec_bytes;
   if (!d->workspace || d->workspace_bytes < need) return GDN_ERR_WORKSPACE;
   if (!prep) g = beta = nullptr;
-  if (!pass) v = nullptr, h0 = nullptr, o = nullptr, hT = nullptr;
+  if (!pass) v = nullptr, pool = StatePool{nullptr, s.N, nullptr}, o = nullptr, hT = nullptr;
 
   const size_t qk_b = (size_t)s.T * s.Hk * gdn::kDim * 2, v_b = (size_t)s.T * s.Hv * gdn::kDim * 2;
-  const size_t gb_b = (size_t)s.T * s.Hv * 4, st_b = (size_t)s.N * s.Hv * gdn::kDim * gdn::kDim * 4;
-  const size_t cu_b = (size_t)(s.N + 1) * 4;
-  const void *a16[] = {q, k, v, o, h0, hT, d->workspace};
+  const size_t gb_b = (size_t)s.T * s.Hv * 4, row_b = (size_t)s.Hv * gdn::kDim * gdn::kDim * 4;
+  const size_t cu_b = (size_t)(s.N + 1) * 4, idx_b = (size_t)s.N * 4;
+  const void *a16[] = {q, k, v, o, pool.h0, hT, d->workspace};
   for (const void *p : a16)
     if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
-  const void *a4[] = {g, beta, cu};
+  const void *a4[] = {g, beta, cu, pool.index};
   for (const void *p : a4)
     if (p && !aligned(p, 4)) return GDN_ERR_ALIGN;
 
-  // The workspace is written by the prep stage and only read by the pass stage.
-  const Range ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {g, gb_b}, {beta, gb_b}, {cu, cu_b}};
-  const Range ro{o, tok ? v_b : 0}, rh{hT, st_b}, rw{d->workspace, need}, rh0{h0, st_b};
-  for (const Range &in : ins)
-    if (overlap(ro, in) || overlap(rh, in) || overlap(rw, in)) return GDN_ERR_ALIAS;
-  if (overlap(ro, rh) || overlap(ro, rw) || overlap(rh, rw) || overlap(ro, rh0) || overlap(rw, rh0))
-    return GDN_ERR_ALIAS;
-  if (hT && h0 && hT != h0 && overlap(rh, rh0)) return GDN_ERR_ALIAS;
-  return GDN_OK;
+  // The workspace is written by the prep stage and only read by the pass stage.  hT may be h0
+  // itself when sequence n reads row n; with an index another sequence may still read the row.
+  const Range outs[] = {{o, tok ? v_b : 0}, {hT, s.N * row_b}, {d->workspace, need}};
+  const Range ins[] = {{q, qk_b},    {k, qk_b}, {v, v_b},
+                       {g, gb_b},    {beta, gb_b}, {cu, cu_b},
+                       {pool.h0, (size_t)pool.rows * row_b}, {pool.index, idx_b}};
+  const InPlace ok[] = {{pool.index ? nullptr : hT, pool.h0}};
+  return check_alias(outs, ins, ok);
 }
 
 // Enqueues the checked stages.
 int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const void *v,
-              const float *g, const float *beta, const int32_t *cu, const float *h0, void *o,
+              const float *g, const float *beta, const int32_t *cu, const StatePool &pool, void *o,
               float *hT, void *ws, hipStream_t stream) {
   unsigned char *rec = static_cast<unsigned char *>(ws);
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
@@ -126,7 +159,8 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
     if (e != hipSuccess) return record_hip(e);
   }
   if (stage & kPass) {
-    gdn::launch_state_pass(q, k, v, cu, h0, o, hT, rec, s.N, s.Hk, s.Hv, stream);
+    gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.N, s.Hk,
+                           s.Hv, stream);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;
@@ -164,19 +198,36 @@ int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const v
                   const float *g, const float *beta, const int32_t *cu_seqlens, const float *h0,
                   void *o, float *hT, void *stream) {
   Shape s;
-  const int st = check_chunk_args(d, s, kBoth, q, k, v, g, beta, cu_seqlens, h0, o, hT);
+  StatePool pool{h0, 0, nullptr};
+  const int st = check_chunk_args(d, s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT);
   if (st != GDN_OK) return st;
-  return run_chunk(s, kBoth, q, k, v, g, beta, cu_seqlens, h0, o, hT, d->workspace,
+  return run_chunk(s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT, d->workspace,
+                   static_cast<hipStream_t>(stream));
+}
+
+int gdn_chunk_fwd_indexed(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, const int32_t *cu_seqlens,
+                          const float *h0, int32_t num_h0, const int32_t *h0_index, void *o,
+                          float *hT, void *stream) {
+  if (!d) return GDN_ERR_NULL;
+  if (!h0 || !h0_index) return GDN_ERR_NULL;
+  if (num_h0 < 1) return GDN_ERR_SHAPE;
+  Shape s;
+  StatePool pool{h0, num_h0, h0_index};
+  const int st = check_chunk_args(d, s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT);
+  if (st != GDN_OK) return st;
+  return run_chunk(s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT, d->workspace,
                    static_cast<hipStream_t>(stream));
 }
 
 int gdn_chunk_prep(const gdn_chunk_desc *d, const void *q, const void *k, const float *g,
                    const float *beta, const int32_t *cu_seqlens, void *stream) {
   Shape s;
-  const int st = check_chunk_args(d, s, kPrep, q, k, nullptr, g, beta, cu_seqlens, nullptr,
+  StatePool pool{nullptr, 0, nullptr};
+  const int st = check_chunk_args(d, s, kPrep, q, k, nullptr, g, beta, cu_seqlens, pool,
                                   nullptr, nullptr);
   if (st != GDN_OK) return st;
-  return run_chunk(s, kPrep, q, k, nullptr, g, beta, cu_seqlens, nullptr, nullptr, nullptr,
+  return run_chunk(s, kPrep, q, k, nullptr, g, beta, cu_seqlens, pool, nullptr, nullptr,
                    d->workspace, static_cast<hipStream_t>(stream));
 }
 
@@ -184,9 +235,10 @@ int gdn_state_pass(const gdn_chunk_desc *d, const void *q, const void *k, const 
                    const int32_t *cu_seqlens, const float *h0, void *o, float *hT,
                    void *stream) {
   Shape s;
-  const int st = check_chunk_args(d, s, kPass, q, k, v, nullptr, nullptr, cu_seqlens, h0, o, hT);
+  StatePool pool{h0, 0, nullptr};
+  const int st = check_chunk_args(d, s, kPass, q, k, v, nullptr, nullptr, cu_seqlens, pool, o, hT);
   if (st != GDN_OK) return st;
-  return run_chunk(s, kPass, q, k, v, nullptr, nullptr, cu_seqlens, h0, o, hT, d->workspace,
+  return run_chunk(s, kPass, q, k, v, nullptr, nullptr, cu_seqlens, pool, o, hT, d->workspace,
                    static_cast<hipStream_t>(stream));
 }
 
@@ -205,7 +257,7 @@ int mixer_layout(const gdn_mixer_desc *d, MixerLayout &m) {
   if (st != GDN_OK) return st;
   if (d->conv_taps != 4) return GDN_ERR_UNSUPPORTED;
   if (!(d->norm_eps > 0.f)) return GDN_ERR_UNSUPPORTED;
-  if ((int64_t)(2 * m.s.Hk + m.s.Hv) * gdn::kDim > INT32_MAX / 2) return GDN_ERR_SHAPE;
+  if (2 * (int64_t)m.s.Hk + m.s.Hv > 65535) return GDN_ERR_SHAPE;  // head segments on grid y
   m.chunk_bytes = m.s.rec_bytes;
   m.q_bytes = round_up((size_t)m.s.T * m.s.Hk * gdn::kDim * 2);
   m.v_bytes = round_up((size_t)m.s.T * m.s.Hv * gdn::kDim * 2);
@@ -220,9 +272,11 @@ size_t gdn_mixer_fwd_workspace_size(const gdn_mixer_desc *d) {
   return m.total;
 }
 
-int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
-                  const float *beta, const void *z, const void *norm_w,
-                  const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream) {
+int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                       const float *g, const float *beta, const void *z, const void *norm_w,
+                       const int32_t *cu_seqlens, const float *h0, const void *conv_in,
+                       int32_t num_states, const int32_t *state_index, void *y, float *hT,
+                       void *conv_out, void *stream) {
   MixerLayout m;
   int st = mixer_layout(d, m);
   if (st != GDN_OK) return st;
@@ -230,32 +284,36 @@ int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, 
   const bool tok = s.T > 0;
   if (!cu_seqlens) return GDN_ERR_NULL;
   if (tok && (!qkv || !conv_w || !g || !beta || !z || !norm_w || !y)) return GDN_ERR_NULL;
+  if (num_states < 1 || (!state_index && num_states != s.N)) return GDN_ERR_SHAPE;
   void *ws = d->chunk.workspace;
   if (!ws || d->chunk.workspace_bytes < m.total) return GDN_ERR_WORKSPACE;
 
+  const int W = d->conv_taps - 1;
   const size_t C = (size_t)(2 * s.Hk + s.Hv) * gdn::kDim;
   const size_t qkv_b = (size_t)s.T * C * 2, cw_b = C * 4 * 2, z_b = (size_t)s.T * s.Hv * gdn::kDim * 2;
-  const size_t gb_b = (size_t)s.T * s.Hv * 4, st_b = (size_t)s.N * s.Hv * gdn::kDim * gdn::kDim * 4;
-  const size_t cu_b = (size_t)(s.N + 1) * 4, nw_b = gdn::kDim * 2;
-  const void *a16[] = {qkv, z, norm_w, y, h0, hT, ws};
+  const size_t gb_b = (size_t)s.T * s.Hv * 4, row_b = (size_t)s.Hv * gdn::kDim * gdn::kDim * 4;
+  const size_t cu_b = (size_t)(s.N + 1) * 4, nw_b = gdn::kDim * 2, win_b = (size_t)W * C * 2;
+  const void *a16[] = {qkv, z, norm_w, y, h0, hT, ws, conv_in, conv_out};
   for (const void *p : a16)
     if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
   const void *a8[] = {conv_w};
   for (const void *p : a8)
     if (p && !aligned(p, 8)) return GDN_ERR_ALIGN;
-  const void *a4[] = {g, beta, cu_seqlens};
+  const void *a4[] = {g, beta, cu_seqlens, state_index};
   for (const void *p : a4)
     if (p && !aligned(p, 4)) return GDN_ERR_ALIGN;
 
-  const Range ins[] = {{qkv, qkv_b}, {conv_w, cw_b}, {g, gb_b}, {beta, gb_b},
-                       {z, z_b},     {norm_w, nw_b}, {cu_seqlens, cu_b}};
-  const Range ry{y, tok ? z_b : 0}, rh{hT, st_b}, rw{ws, m.total}, rh0{h0, st_b};
-  for (const Range &in : ins) {
-    if (overlap(ry, in) || overlap(rh, in) || overlap(rw, in)) return GDN_ERR_ALIAS;
-  }
-  if (overlap(ry, rh) || overlap(ry, rw) || overlap(rh, rw) || overlap(ry, rh0) || overlap(rw, rh0))
-    return GDN_ERR_ALIAS;
-  if (hT && h0 && hT != h0 && overlap(rh, rh0)) return GDN_ERR_ALIAS;
+  // In place (hT == h0, conv_out == conv_in) only when sequence n continues from state n.
+  const Range outs[] = {{y, tok ? z_b : 0}, {hT, s.N * row_b}, {conv_out, s.N * win_b},
+                        {ws, m.total}};
+  const Range ins[] = {{qkv, qkv_b},       {conv_w, cw_b},
+                       {g, gb_b},          {beta, gb_b},
+                       {z, z_b},           {norm_w, nw_b},
+                       {cu_seqlens, cu_b}, {h0, (size_t)num_states * row_b},
+                       {conv_in, (size_t)num_states * win_b}, {state_index, (size_t)s.N * 4}};
+  const InPlace ok[] = {{state_index ? nullptr : hT, h0}, {state_index ? nullptr : conv_out, conv_in}};
+  st = check_alias(outs, ins, ok);
+  if (st != GDN_OK) return st;
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   unsigned char *base = static_cast<unsigned char *>(ws);
@@ -265,17 +323,34 @@ int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, 
   unsigned char *op = vp + m.v_bytes;
   (void)hipGetLastError();
   if (tok) {
-    gdn::launch_mixer_prep(qkv, conv_w, cu_seqlens, s.T, s.N, s.Hk, s.Hv, qp, kp, vp, strm);
+    gdn::launch_mixer_prep(qkv, conv_w, cu_seqlens, s.T, s.N, s.Hk, s.Hv, conv_in, state_index,
+                           num_states, qp, kp, vp, strm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
   }
-  st = run_chunk(s, kBoth, qp, kp, vp, g, beta, cu_seqlens, h0, op, hT, base, strm);
+  // after the prep, which reads conv_in: conv_out may be conv_in itself
+  if (conv_out) {
+    gdn::launch_conv_window_out(qkv, cu_seqlens, s.N, (int)C, conv_in, state_index, num_states,
+                                conv_out, strm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip(e);
+  }
+  const StatePool pool{h0, num_states, state_index};
+  st = run_chunk(s, kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm);
   if (st != GDN_OK) return st;
   if (tok) {
     gdn::launch_gated_rmsnorm(op, z, norm_w, d->norm_eps, s.T, s.Hv, y, strm);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;
+}
+
+int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
+                  const float *beta, const void *z, const void *norm_w,
+                  const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream) {
+  if (!d) return GDN_ERR_NULL;
+  return gdn_mixer_fwd_cont(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, nullptr,
+                            d->chunk.num_seqs, nullptr, y, hT, nullptr, stream);
 }
 
 }  // extern "C"

@@ -20,14 +20,24 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// Start token of the sequence that contains token t (cu is monotone, cu[0] = 0).
-__device__ __forceinline__ int seq_start(const int32_t *__restrict__ cu, int N, int t) {
-  int lo = 0, hi = N - 1;  // largest n with cu[n] <= t
+// Index of the sequence that contains token t: the largest n with cu[n] <= t (cu is monotone,
+// cu[0] = 0; of several empty sequences starting at t the last one, which owns the token).
+__device__ __forceinline__ int seq_of(const int32_t *__restrict__ cu, int N, int t) {
+  int lo = 0, hi = N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (cu[mid] <= t) lo = mid; else hi = mid - 1;
   }
-  return cu[lo];
+  return lo;
+}
+
+// Carried conv window of sequence n ([W, C] bf16, oldest row first), or null for zeros.
+__device__ __forceinline__ const unsigned short *window_of(const unsigned short *conv_in,
+                                                           const int32_t *state_index,
+                                                           int num_states, int n, size_t rows) {
+  if (!conv_in) return nullptr;
+  const int r = state_index ? state_index[n] : n;
+  return (r >= 0 && r < num_states) ? conv_in + (size_t)r * rows : nullptr;
 }
 
 }  // namespace
@@ -35,10 +45,13 @@ __device__ __forceinline__ int seq_start(const int32_t *__restrict__ cu, int N, 
 // Grid: (ceil(T / 64), 2 Hk + Hv).  Block y selects a 128-channel head segment of the packed
 // q | k | v channels; each thread owns 8 channels x 4 tokens.  Lanes 16m .. 16m+15 of a wave hold
 // the 16 channel groups of the same tokens, so the per-token L2 norm is a 16-lane butterfly.
+// The conv reads the carried window (conv_in, [W = 3, C] per state) for the positions before a
+// sequence's first token, zeros when there is none.
 __global__ __launch_bounds__(256) void mixer_prep_kernel(
     const unsigned short *__restrict__ qkv, const unsigned short *__restrict__ conv_w,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv,
-    unsigned short *__restrict__ qo, unsigned short *__restrict__ ko,
+    const unsigned short *__restrict__ conv_in, const int32_t *__restrict__ state_index,
+    int num_states, unsigned short *__restrict__ qo, unsigned short *__restrict__ ko,
     unsigned short *__restrict__ vo) {
   const int seg = blockIdx.y;                  // 0..Hk-1: q heads, Hk..2Hk-1: k heads, then v heads
   const int C = (2 * Hk + Hv) * kDim;
@@ -65,12 +78,18 @@ __global__ __launch_bounds__(256) void mixer_prep_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (valid) {
-      const int ss = seq_start(cu, N, t);
+      const int n = seq_of(cu, N, t);
+      const int ss = cu[n];
+      const unsigned short *win =
+          t - 3 < ss ? window_of(conv_in, state_index, num_states, n, (size_t)3 * C) : nullptr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int src = t - 3 + j;
-        if (src >= ss) {
-          const u16x8 xv = *reinterpret_cast<const u16x8 *>(qkv + (size_t)src * C + ch0);
+        const unsigned short *x = src >= ss ? qkv + (size_t)src * C
+                                  : win     ? win + (size_t)(src - ss + 3) * C
+                                            : nullptr;
+        if (x) {
+          const u16x8 xv = *reinterpret_cast<const u16x8 *>(x + ch0);
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] += wt[e][j] * bits_to_float(xv[e]);
         }
@@ -129,14 +148,58 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(
   if (valid) *reinterpret_cast<u16x8 *>(y + off) = out;
 }
 
+// conv_out[n] = the last 3 rows of sequence n's input stream (its carried window, or zeros,
+// followed by its tokens), bit for bit.  Grid (N, ceil(C / 8 / 256)); a thread moves 8 channels
+// of all 3 rows and reads them all before it writes, so conv_out may be conv_in itself when
+// sequence n reads window n.
+__global__ __launch_bounds__(256) void conv_window_out_kernel(
+    const unsigned short *__restrict__ qkv, const int32_t *__restrict__ cu, int C,
+    const unsigned short *conv_in, const int32_t *__restrict__ state_index, int num_states,
+    unsigned short *conv_out) {
+  const int n = blockIdx.x;
+  const int ch = 8 * (blockIdx.y * 256 + threadIdx.x);
+  if (ch >= C) return;
+  const int tb = cu[n], te = cu[n + 1];
+  const unsigned short *win = window_of(conv_in, state_index, num_states, n, (size_t)3 * C);
+  u16x8 rows[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int p = te - 3 + j;  // stream position, >= tb - 3
+    const unsigned short *x = p >= tb ? qkv + (size_t)p * C
+                              : win   ? win + (size_t)(p - tb + 3) * C
+                                      : nullptr;
+    if (x) {
+      rows[j] = *reinterpret_cast<const u16x8 *>(x + ch);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rows[j][e] = 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    *reinterpret_cast<u16x8 *>(conv_out + ((size_t)n * 3 + j) * C + ch) = rows[j];
+}
+
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
-                       int Hk, int Hv, void *q, void *k, void *v, hipStream_t stream) {
+                       int Hk, int Hv, const void *conv_in, const int32_t *state_index,
+                       int num_states, void *q, void *k, void *v, hipStream_t stream) {
   dim3 grid((unsigned)((T + 63) / 64), (unsigned)(2 * Hk + Hv));
   hipLaunchKernelGGL(mixer_prep_kernel, grid, dim3(256), 0, stream,
                      static_cast<const unsigned short *>(qkv),
                      static_cast<const unsigned short *>(conv_w), cu, (int)T, N, Hk, Hv,
+                     static_cast<const unsigned short *>(conv_in), state_index, num_states,
                      static_cast<unsigned short *>(q), static_cast<unsigned short *>(k),
                      static_cast<unsigned short *>(v));
+}
+
+void launch_conv_window_out(const void *qkv, const int32_t *cu, int N, int C, const void *conv_in,
+                            const int32_t *state_index, int num_states, void *conv_out,
+                            hipStream_t stream) {
+  dim3 grid((unsigned)N, (unsigned)((C / 8 + 255) / 256));
+  hipLaunchKernelGGL(conv_window_out_kernel, grid, dim3(256), 0, stream,
+                     static_cast<const unsigned short *>(qkv), cu, C,
+                     static_cast<const unsigned short *>(conv_in), state_index, num_states,
+                     static_cast<unsigned short *>(conv_out));
 }
 
 void launch_gated_rmsnorm(const void *o, const void *z, const void *norm_w, float eps, int64_t T,

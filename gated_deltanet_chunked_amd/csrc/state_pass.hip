@@ -433,7 +433,8 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
 __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
-    const float *h0, unsigned short *__restrict__ o, float *hT,  // hT may equal h0
+    const float *h0, const int32_t *__restrict__ h0_index, int num_h0,
+    unsigned short *__restrict__ o, float *hT,  // hT may equal h0 when h0_index is NULL
     const uint8_t *__restrict__ rec, int Hk, int Hv) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char recs[kRecStages * kRecBytes];
@@ -564,14 +565,20 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     return;
   }
 
-  // State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].
+  // State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].  Sequence n starts
+  // from initial state h0_index[n] of the pool (zeros outside [0, num_h0)), or from state n.
+  const float *h0s = nullptr;
+  if (h0) {
+    const int r = h0_index ? h0_index[n] : n;
+    if (r >= 0 && r < num_h0) h0s = h0 + ((size_t)r * Hv + h) * kDim * kDim;
+  }
   f32x4 H[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int key = state_key(w, a, 4 * lg + rr);
-      H[a][rr] = h0 ? h0[state_base + (size_t)key * kDim + d0 + lj] : 0.f;
+      H[a][rr] = h0s ? h0s[(size_t)key * kDim + d0 + lj] : 0.f;
     }
 
   if (nc > 0) {
@@ -610,12 +617,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
 }
 
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
-                       const float *h0, void *o, float *hT, const void *rec, int N, int Hk, int Hv,
-                       hipStream_t stream) {
+                       const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
+                       const void *rec, int N, int Hk, int Hv, hipStream_t stream) {
   const unsigned nblocks = (unsigned)N * (unsigned)Hv * kDvTiles;
   hipLaunchKernelGGL(state_pass_kernel, dim3(nblocks), dim3(kThreads), 0, stream,
                      static_cast<const unsigned short *>(q), static_cast<const unsigned short *>(k),
-                     static_cast<const unsigned short *>(v), cu, h0,
+                     static_cast<const unsigned short *>(v), cu, h0, h0_index, num_h0,
                      static_cast<unsigned short *>(o), hT, static_cast<const uint8_t *>(rec), Hk, Hv);
 }
 

@@ -165,3 +165,19 @@ def make_mixer_inputs(seed: int, lengths=(MIXER_T,), Hk: int = 16, Hv: int = 32,
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     h0 = (0.05 * rng.standard_normal((len(lengths), Hv, d, d))).astype(np.float32) if with_h0 else None
     return MixerInputs(qkv, conv_w, beta, g, z, norm_w, cu, h0)
+
+
+# ----------------------------------------------------------------------------------------------
+# Carried states for continuation: pools of initial recurrent states and conv input windows.
+# ----------------------------------------------------------------------------------------------
+def make_state_pool(seed: int, S: int, Hv: int, d: int = D, std: float = 0.05) -> np.ndarray:
+    """S initial states, fp32 [S, Hv, d, d] ~ std N(0,1) (key-major, as h0)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (std * rng.standard_normal((S, Hv, d, d))).astype(np.float32)
+
+
+def make_window_pool(seed: int, S: int, C: int, taps: int = 4) -> np.ndarray:
+    """S conv input windows, bf16 bits [S, taps-1, C] ~ N(0,1) (qkv rows, oldest first)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return bf16_bits(rng.standard_normal((S, taps - 1, C)))
+

@@ -110,14 +110,33 @@ GDN_EXPORT int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void 
                   void *o, float *hT, void *stream);
 
 /*
+ * gdn_chunk_fwd with the initial states drawn from a pool by index: one prefix's final state
+ * handed to each of several candidates without copying it ("open-jev-fast" README, "Phase 2"
+ * item 2; PR #186, "Review scope and map", per-candidate state).
+ *   h0       : fp32 [num_h0, Hv, dk, dv] (device), num_h0 >= 1
+ *   h0_index : int32 [N] (device).  Sequence n starts from h0[h0_index[n]]; an index outside
+ *              [0, num_h0) means a zero state (the library cannot check device values, so an
+ *              out-of-range index is defined rather than an error).
+ * Other arguments as gdn_chunk_fwd; the workspace size is gdn_chunk_fwd_workspace_size().
+ * Errors: GDN_ERR_NULL if h0 or h0_index is NULL, GDN_ERR_SHAPE if num_h0 < 1, GDN_ERR_ALIAS if
+ * hT overlaps h0 at all (other sequences may still read the row), or if an output overlaps
+ * h0_index; GDN_ERR_ALIGN if h0_index is not 4-byte aligned.
+ */
+GDN_EXPORT int gdn_chunk_fwd_indexed(const gdn_chunk_desc *d, const void *q, const void *k,
+                                     const void *v, const float *g, const float *beta,
+                                     const int32_t *cu_seqlens, const float *h0, int32_t num_h0,
+                                     const int32_t *h0_index, void *o, float *hT, void *stream);
+
+/*
  * The two stages of gdn_chunk_fwd, callable on their own (gdn_chunk_fwd = gdn_chunk_prep, then
  * gdn_state_pass, on one stream with one workspace).  The "open-jev-fast" README ("Phase 3",
  * item 1) separates the work that does not depend on the recurrent state, which runs for many
  * chunks side by side, from the state that is passed chunk to chunk.
  *
- * gdn_chunk_prep: for every (chunk, k-head) in parallel -- local cumsum of g, K K^T and Q K^T,
- *   A = beta_i e^{G_i - G_j} k_i.k_j (i > j), T = (I + A)^-1 -- writes T diag(beta), the masked
- *   decayed Q K^T, the decays and K^T into the workspace.  Reads q, k, g, beta, cu_seqlens.
+ * gdn_chunk_prep: for every (chunk, v-head) in parallel -- local cumsum of g, K K^T and Q K^T,
+ *   A = beta_i e^{G_i - G_j} k_i.k_j (i > j), T = (I + A)^-1 -- writes one record per (chunk,
+ *   v-head) into the workspace: T diag(beta), the masked decayed Q K^T and the decays.  Reads q,
+ *   k, g, beta, cu_seqlens.
  * gdn_state_pass: for every (sequence, v-head, 16 value columns) in parallel, walks the chunks
  *   in order with the fp32 state on chip, writing o and hT.  Reads q, k, v, cu_seqlens, h0 and
  *   the workspace exactly as gdn_chunk_prep left it for the same inputs and shapes.
@@ -154,6 +173,33 @@ GDN_EXPORT size_t gdn_mixer_fwd_workspace_size(const gdn_mixer_desc *d);
 GDN_EXPORT int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
                   const float *beta, const void *z, const void *norm_w,
                   const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream);
+
+/*
+ * The mixer continuing from carried states: beside the recurrent state, each sequence carries
+ * the conv input window -- the last conv_taps - 1 rows of qkv before it -- so that a prefix's
+ * window and state can be handed on to the candidates that continue it ("open-jev-fast" README,
+ * "Phase 2" item 2).  C = 2*Hk*dk + Hv*dv, W = conv_taps - 1 (= 3).
+ *   h0       : fp32 [num_states, Hv, dk, dv] or NULL (zero states)
+ *   conv_in  : bf16 [num_states, W, C] or NULL (zeros before every sequence), oldest row first:
+ *              row W-1 is the input just before the sequence's first token
+ *   state_index : int32 [N] or NULL.  Sequence n continues from state and window
+ *              state_index[n]; an index outside [0, num_states) means zeros.  NULL: sequence n
+ *              continues from state n, and num_states must be N.
+ *   hT       : fp32 [N, Hv, dk, dv] or NULL;  conv_out : bf16 [N, W, C] or NULL -- the last W
+ *              rows of sequence n's input stream (its window followed by its tokens), copied
+ *              bit for bit: the window the next call continues from.
+ * gdn_mixer_fwd is this with conv_in, state_index and conv_out NULL.  hT == h0 and conv_out ==
+ * conv_in (in-place continuation) are allowed when state_index is NULL; with an index any
+ * overlap of an output with a pool is GDN_ERR_ALIAS.  conv_in and conv_out need 16-byte
+ * alignment, state_index 4.  GDN_ERR_SHAPE if num_states < 1, or num_states != N without an
+ * index.  Workspace: gdn_mixer_fwd_workspace_size().
+ */
+GDN_EXPORT int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                                  const float *g, const float *beta, const void *z,
+                                  const void *norm_w, const int32_t *cu_seqlens, const float *h0,
+                                  const void *conv_in, int32_t num_states,
+                                  const int32_t *state_index, void *y, float *hT, void *conv_out,
+                                  void *stream);
 
 #ifdef __cplusplus
 }

@@ -165,6 +165,68 @@ def test_mixer_validation():
     assert call(good(), y=a["v"]) == gdn.GDN_ERR_ALIAS          # y over z
 
 
+def _call_indexed(num_h0=3, idx=None, **over):
+    a = _addrs()
+    a["idx"] = a["cu"] + GB // 2
+    a.update(over)
+    if idx is not None:
+        a["idx"] = idx
+    ws_bytes = gdn.gdn_chunk_fwd_workspace_size(T, N, HK, HV)
+    d = gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], ws_bytes)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return gdn.lib().gdn_chunk_fwd_indexed(ctypes.byref(d), P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]),
+                                           P(a["beta"]), P(a["cu"]), P(a["h0"]), num_h0, P(a["idx"]), P(a["o"]),
+                                           P(a["hT"]), None)
+
+
+def test_indexed_validation():
+    a = _addrs()
+    row = HV * 128 * 128 * 4
+    idx = a["cu"] + GB // 2
+    assert _call_indexed(h0=None) == gdn.GDN_ERR_NULL           # a pool is required
+    assert _call_indexed(idx=0) == gdn.GDN_ERR_NULL             # NULL index
+    assert _call_indexed(num_h0=0) == gdn.GDN_ERR_SHAPE
+    assert _call_indexed(num_h0=-2) == gdn.GDN_ERR_SHAPE
+    assert _call_indexed(idx=idx + 2) == gdn.GDN_ERR_ALIGN
+    assert _call_indexed(h0=a["h0"] + 4) == gdn.GDN_ERR_ALIGN
+    assert _call_indexed(hT=a["h0"]) == gdn.GDN_ERR_ALIAS       # no in-place with an index
+    assert _call_indexed(hT=a["h0"] + 2 * row) == gdn.GDN_ERR_ALIAS   # row 2 of a 3-row pool
+    assert _call_indexed(o=idx - 256) == gdn.GDN_ERR_ALIAS      # o over the index
+    assert _call_indexed(q=None) == gdn.GDN_ERR_NULL
+
+
+def test_mixer_cont_validation():
+    a = _addrs()
+    ws = gdn.gdn_mixer_fwd_workspace_size(T, N, HK, HV)
+    C = (2 * HK + HV) * 128
+    P = ctypes.c_void_p
+    extra = a["cu"] + GB // 2  # room for the index and the windows, each under 1 MiB
+
+    def call(S=N, **over):
+        b = {"qkv": a["q"], "cw": a["k"], "g": a["g"], "beta": a["beta"], "z": a["v"], "nw": a["h0"] + GB // 2,
+             "cu": a["cu"], "h0": a["h0"], "cin": extra, "idx": None, "y": a["o"], "hT": a["hT"],
+             "cout": extra + (1 << 20)}
+        b.update(over)
+        pp = lambda x: None if x is None else P(x)
+        m = gdn.MixerDesc(gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], ws), 4, 1e-6)
+        return gdn.lib().gdn_mixer_fwd_cont(ctypes.byref(m), pp(b["qkv"]), pp(b["cw"]), pp(b["g"]), pp(b["beta"]),
+                                            pp(b["z"]), pp(b["nw"]), pp(b["cu"]), pp(b["h0"]), pp(b["cin"]), S,
+                                            pp(b["idx"]), pp(b["y"]), pp(b["hT"]), pp(b["cout"]), None)
+
+    idx = extra + (2 << 20)
+    assert call(S=2) == gdn.GDN_ERR_SHAPE                        # pool size must be N without an index
+    assert call(S=0, idx=idx) == gdn.GDN_ERR_SHAPE
+    assert call(cin=extra + 8) == gdn.GDN_ERR_ALIGN
+    assert call(cout=extra + (1 << 20) + 4) == gdn.GDN_ERR_ALIGN
+    assert call(S=2, idx=idx + 1) == gdn.GDN_ERR_ALIGN
+    assert call(S=2, idx=idx, cout=extra) == gdn.GDN_ERR_ALIAS  # in-place window with an index
+    assert call(S=2, idx=idx, hT=a["h0"]) == gdn.GDN_ERR_ALIAS  # in-place state with an index
+    assert call(cout=extra + 3 * C) == gdn.GDN_ERR_ALIAS         # partial overlap with conv_in
+    assert call(cout=a["o"]) == gdn.GDN_ERR_ALIAS                # two outputs overlap
+    assert call(y=idx, S=2, idx=idx) == gdn.GDN_ERR_ALIAS        # y over the index
+    assert call(z=None) == gdn.GDN_ERR_NULL
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(gdn, "_lib_handle", None)
