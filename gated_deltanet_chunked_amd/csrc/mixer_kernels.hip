@@ -3,32 +3,30 @@
 // The "open-jev-fast" README ("Phase 2", item 1) fuses the Gated DeltaNet input prep (causal
 // conv, SiLU, q/k/v split, L2 norm) into one kernel and the gated RMSNorm into another; "Phase 3"
 // item 3 computes q/k at the 16 key heads.  Both kernels here are HBM-bound streams: 16-byte
-// vector loads and stores, fp32 math, and the per-row reductions as 16-lane butterflies inside a
-// wave (no LDS).
+// vector loads and stores, fp32 math (SiLU and the norms' reciprocal square roots on the hardware
+// exp2 / rcp / rsq units: the outputs are bf16), and the per-row reductions as 16-lane
+// butterflies inside a wave (no LDS).
 #include "gdn_device.h"
 
 namespace gdn {
 
 namespace {
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+// x sigmoid(x) with the hardware exp2 and reciprocal (each about 1 ulp): the result is rounded
+// to bf16 (8 bits) right after, far above their error.  Saturates correctly: exp2 overflows to
+// inf for x << 0 (result -0), underflows to 0 for x >> 0 (result x).
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+// 1 / sqrt(x) for x > 0 with the hardware reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
 
 __device__ __forceinline__ float sum16(float x) {
   // butterfly over the 16 lanes that share l / 16
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
-}
-
-// Index of the sequence that contains token t: the largest n with cu[n] <= t (cu is monotone,
-// cu[0] = 0; of several empty sequences starting at t the last one, which owns the token).
-__device__ __forceinline__ int seq_of(const int32_t *__restrict__ cu, int N, int t) {
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 // Carried conv window of sequence n ([W, C] bf16, oldest row first), or null for zeros.
@@ -42,22 +40,40 @@ __device__ __forceinline__ const unsigned short *window_of(const unsigned short 
 
 }  // namespace
 
-// Grid: (ceil(T / 64), 2 Hk + Hv).  Block y selects a 128-channel head segment of the packed
-// q | k | v channels; each thread owns 8 channels x 4 tokens.  Lanes 16m .. 16m+15 of a wave hold
-// the 16 channel groups of the same tokens, so the per-token L2 norm is a 16-lane butterfly.
-// The conv reads the carried window (conv_in, [W = 3, C] per state) for the positions before a
-// sequence's first token, zeros when there is none.
+// Grid: (ceil(T / (16 kPrepTokens)), 2 Hk + Hv).  Block y selects a 128-channel head segment of
+// the packed q | k | v channels; each thread owns 8 channels x kPrepTokens consecutive tokens.
+// Lanes 16m .. 16m+15 of a wave hold the 16 channel groups of the same tokens, so the per-token
+// L2 norm is a 16-lane butterfly.
+//
+// A thread loads the kPrepTokens + 3 input rows its conv window slides over all at once (one
+// round trip to memory instead of one per tap), and finds the sequence of each of its tokens by
+// binary searches over cu_seqlens run side by side.  Positions before a sequence's first token
+// read the carried window (conv_in, [3, C] per state), or zeros when there is none.
+constexpr int kPrepTokens = 2;
+
 __global__ __launch_bounds__(256) void mixer_prep_kernel(
     const unsigned short *__restrict__ qkv, const unsigned short *__restrict__ conv_w,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv,
     const unsigned short *__restrict__ conv_in, const int32_t *__restrict__ state_index,
     int num_states, unsigned short *__restrict__ qo, unsigned short *__restrict__ ko,
     unsigned short *__restrict__ vo) {
+  constexpr int P = kPrepTokens;
   const int seg = blockIdx.y;                  // 0..Hk-1: q heads, Hk..2Hk-1: k heads, then v heads
   const int C = (2 * Hk + Hv) * kDim;
   const int tid = threadIdx.x, chg = tid & 15, tg = tid >> 4;  // channel group, token group
   const int ch0 = seg * kDim + chg * 8;
   const bool is_qk = seg < 2 * Hk;
+  const int t0 = (blockIdx.x * 16 + tg) * P;
+
+  // input rows t0 - 3 .. t0 + P - 1, clamped into [0, T - 1]: a clamped row is never used
+  // (a row before 0 or before a sequence start fails src >= ss; a row past T - 1 only serves
+  // tokens past the end)
+  u16x8 xr[P + 3];
+#pragma unroll
+  for (int r = 0; r < P + 3; ++r) {
+    const int row = min(max(t0 - 3 + r, 0), T - 1);
+    xr[r] = *reinterpret_cast<const u16x8 *>(qkv + (size_t)row * C + ch0);
+  }
 
   // conv weights of my 8 channels: w[ch][0..3], tap 3 multiplies the current token
   float wt[8][4];
@@ -69,27 +85,47 @@ __global__ __launch_bounds__(256) void mixer_prep_kernel(
     for (int j = 0; j < 4; ++j) wt[e][j] = bits_to_float(wv[j]);
   }
 
-  const int tbase = blockIdx.x * 64 + tg * 4;
+  // sequence of token t0 + u: the largest n with cu[n] <= t (cu[0] = 0); ss = cu[n].  Every
+  // search runs the same ceil(log2 N) steps; each step halves the range [lo, hi].
+  int lo[P], hi[P], ss[P];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = tbase + u;
+  for (int u = 0; u < P; ++u) lo[u] = 0, hi[u] = N - 1, ss[u] = 0;
+  const int steps = N > 1 ? 32 - __clz(N - 1) : 0;
+  for (int st = 0; st < steps; ++st) {
+    int mid[P], cm[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      mid[u] = (lo[u] + hi[u] + 1) >> 1;  // lo <= mid <= hi <= N - 1
+      cm[u] = cu[mid[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if (lo[u] < hi[u]) {
+        if (cm[u] <= t0 + u) lo[u] = mid[u], ss[u] = cm[u];
+        else hi[u] = mid[u] - 1;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    const int t = t0 + u;
     const bool valid = t < T;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (valid) {
-      const int n = seq_of(cu, N, t);
-      const int ss = cu[n];
       const unsigned short *win =
-          t - 3 < ss ? window_of(conv_in, state_index, num_states, n, (size_t)3 * C) : nullptr;
+          t - 3 < ss[u] ? window_of(conv_in, state_index, num_states, lo[u], (size_t)3 * C) : nullptr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int src = t - 3 + j;
-        const unsigned short *x = src >= ss ? qkv + (size_t)src * C
-                                  : win     ? win + (size_t)(src - ss + 3) * C
-                                            : nullptr;
-        if (x) {
-          const u16x8 xv = *reinterpret_cast<const u16x8 *>(x + ch0);
+        u16x8 xv;
+        bool have = true;
+        if (src >= ss[u]) xv = xr[u + j];
+        else if (win) xv = *reinterpret_cast<const u16x8 *>(win + (size_t)(src - ss[u] + 3) * C + ch0);
+        else have = false;
+        if (have) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] += wt[e][j] * bits_to_float(xv[e]);
         }
@@ -102,7 +138,7 @@ __global__ __launch_bounds__(256) void mixer_prep_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss2 += acc[e] * acc[e];
       ss2 = sum16(ss2);
-      const float rn = 1.f / sqrtf(ss2 + 1e-6f);
+      const float rn = rsqrt_hw(ss2 + 1e-6f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] *= rn;
     }
@@ -138,7 +174,7 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(
     ss += of[e] * of[e];
   }
   ss = sum16(ss);
-  const float r = 1.f / sqrtf(ss * (1.f / kDim) + eps);
+  const float r = rsqrt_hw(ss * (1.f / kDim) + eps);
   u16x8 out;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -183,7 +219,7 @@ __global__ __launch_bounds__(256) void conv_window_out_kernel(
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, const void *conv_in, const int32_t *state_index,
                        int num_states, void *q, void *k, void *v, hipStream_t stream) {
-  dim3 grid((unsigned)((T + 63) / 64), (unsigned)(2 * Hk + Hv));
+  dim3 grid((unsigned)((T + 16 * kPrepTokens - 1) / (16 * kPrepTokens)), (unsigned)(2 * Hk + Hv));
   hipLaunchKernelGGL(mixer_prep_kernel, grid, dim3(256), 0, stream,
                      static_cast<const unsigned short *>(qkv),
                      static_cast<const unsigned short *>(conv_w), cu, (int)T, N, Hk, Hv,
