@@ -52,18 +52,21 @@ constexpr int kOutputWave0 = kComputeWaves + kProducerWaves;
 constexpr int kPrefetchWave = kOutputWave0 + kOutputWaves;
 constexpr int kThreads = 64 * (kPrefetchWave + 1);
 constexpr int kPrefetchAhead = 6;     // chunks between the L2 warm-up of a chunk and its use
-// Tile ring slot: K tile | Q tile (64 x 128 bf16 each, swizzled) | V tile (64 x 16 bf16).
-constexpr int kTileStages = 2;
+// Tile ring slot: K tile | Q tile (64 x 128 bf16 each, swizzled) | V tile (64 x 16 bf16) |
+// T' hi and lo fragments of the record (12 KiB, as stored).
+constexpr int kTileStages = 3;
 constexpr int kTK = 0;
 constexpr int kTQ = kTK + kChunk * kDim * 2;              // 16384
 constexpr int kTV = kTQ + kChunk * kDim * 2;              // 32768
-constexpr int kTileBytes = kTV + kChunk * kDvTile * 2;    // 34816
-constexpr int kRecStages = 3;                             // record ring slot: kRecBytes
+constexpr int kTT = kTV + kChunk * kDvTile * 2;           // 34816
+constexpr int kTpBytes = kRecP - kRecTpHi;                // 12288
+constexpr int kTileBytes = kTT + kTpBytes;                // 47104
 constexpr int kOBytes = 16 * kDvTile * 2;                 // one row block's 16 output rows
+constexpr int kDecBytes = kRecBytes - kRecEG;             // e^G and e^{G_last - G}: 512
+constexpr int kDecStages = 3;                             // decay ring slots
 constexpr int kDmaTile = kChunk * kDim * 2 / 1024;        // 16 instructions of 1 KiB (K or Q)
-constexpr int kDmaRec = (kRecBytes + 1023) / 1024;        // 19 (the last one half full)
 constexpr int kDmaV = kChunk * kDvTile * 2 / 1024;        // 2
-static_assert(kTileBytes % 16 == 0 && kRecBytes % 16 == 0 && kTV % 16 == 0, "16-byte LDS slots");
+static_assert(kTileBytes % 16 == 0 && kTV % 16 == 0, "16-byte LDS slots");
 
 // Byte offset of bf16 element (row, col) in a swizzled 64 x 128 tile: 16-byte chunks are
 // XOR-permuted by row so that 16 lanes reading one chunk column of 16 rows hit distinct banks.
@@ -138,16 +141,17 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const void *p) {
 }
 
 // Producers.  Per chunk the four producer waves issue the K and Q tiles (16 instructions each),
-// the record (19, the last one half full) and the V tile (2).  Wave pw's share is fixed -- tile
-// rows 4m .. 4m + 3 and record KiB m for m = pw mod 4, and the V tile on wave 3 -- so the vmcnt
-// bookkeeping is static.  Rows past the sequence end are clamped to its last row, which the
-// compute waves never use.
-__host__ __device__ constexpr int kRecA(int pw) { return 2; }                  // KiB pw, pw + 4
-__host__ __device__ constexpr int kRecB(int pw) { return pw < 3 ? 3 : 2; }     // pw + 8, + 12, + 16
-__host__ __device__ constexpr int kTileCount(int pw) { return 8 + (pw == 3 ? kDmaV : 0); }
-__host__ __device__ constexpr int kChunkCount(int pw) { return kRecA(pw) + kRecB(pw) + kTileCount(pw); }
-static_assert(kChunkCount(0) + kChunkCount(1) + kChunkCount(2) + kChunkCount(3) ==
-                  2 * kDmaTile + kDmaRec + kDmaV, "every load has an owner");
+// the V tile (2), the T' fragments of the record (12) and its decays (one, half a wave).  Wave pw's share is fixed -- tile rows 4m .. 4m + 3 for m = pw mod 4, and
+// the V tile on wave 3 -- so the vmcnt bookkeeping is static.  Rows past the sequence end are
+// clamped to its last row, which the compute waves never use.
+constexpr int kDmaTp = kTpBytes / 1024;                   // 12: T' KiB m on wave m % 4
+__host__ __device__ constexpr int kTileCount(int pw) { return 8 + kDmaTp / 4 + (pw == 3 ? kDmaV : 0); }
+static_assert(kTileCount(0) + kTileCount(1) + kTileCount(2) + kTileCount(3) ==
+                  2 * kDmaTile + kDmaV + kDmaTp, "every load has an owner");
+static_assert(kRecTpLo == kRecTpHi + kTpBytes / 2 && kDmaTp % 4 == 0, "T' hi | lo contiguous");
+// Producer wave kDecWave also loads the chunk's decays (one half-wave instruction).
+constexpr int kDecWave = 1;
+__host__ __device__ constexpr int kChunkCount(int pw) { return kTileCount(pw) + (pw == kDecWave ? 1 : 0); }
 
 // Per-lane byte offsets of a producer wave's loads, fixed for the whole sequence.  Tile
 // instruction i of wave pw covers tile rows 16 i + 4 pw .. + 3 (lane l: row 16 i + 4 pw + l / 16,
@@ -157,65 +161,86 @@ static_assert(kChunkCount(0) + kChunkCount(1) + kChunkCount(2) + kChunkCount(3) 
 struct ProducerLanes {
   uint32_t tile;  // (4 pw + l / 16) * row stride + 16 * lc
   uint32_t v;     // (l / 2) * Hv * 256 + 2 * (d0 + 8 (l % 2))
-  uint32_t rec;   // 16 l
   int lc, row0;   // for the clamped last chunk
 };
 
-// K, Q and V tiles of chunk c into a tile ring slot (kTileCount(pw) instructions).  kb, qb and vb
-// point at row 0 of this workgroup's head in bytes; rows past the sequence end are clamped to its
-// last row, which the compute waves never use.
+// Part 0 (K), 1 (Q) or 2 (V, wave 3 only) of the tiles of chunk c into a tile ring slot, with
+// one KiB of the chunk's T' fragments (tp: its record): 5, 5 and 1 (+ kDmaV) instructions.  kb,
+// qb and vb point at row 0 of this workgroup's head in bytes; rows past the sequence end are
+// clamped to its last row, which the compute waves never use.
+template <int Part>
 __device__ __forceinline__ void dma_tiles(int c, int tb, int te, int Hk, int Hv, int pw, int l,
                                           const unsigned char *kb, const unsigned char *qb,
-                                          const unsigned char *vb, const ProducerLanes &pl,
-                                          unsigned slot) {
+                                          const unsigned char *vb, const uint8_t *tp,
+                                          const ProducerLanes &pl, unsigned slot) {
   const int t0 = tb + kChunk * c;
   const int L = min(kChunk, te - t0);
   const size_t rs = (size_t)Hk * kDim * 2, vrs = (size_t)Hv * kDim * 2;
-  const unsigned char *kc = kb + (size_t)t0 * rs, *qc = qb + (size_t)t0 * rs, *vc = vb + (size_t)t0 * vrs;
-  if (L == kChunk) {
+  // T' KiB pw + 4 Part of this chunk's record
+  dma16s(tp + (pw + 4 * Part) * 1024, 16 * l, slot + kTT + (pw + 4 * Part) * 1024);
+  if (Part < 2) {
+    const unsigned char *base = (Part == 0 ? kb : qb) + (size_t)t0 * rs;
+    const unsigned dst = slot + (Part == 0 ? kTK : kTQ);
+    if (L == kChunk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16s(kc + 16 * i * rs, pl.tile, slot + kTK + (4 * i + pw) * 1024);
+      for (int i = 0; i < 4; ++i) dma16s(base + 16 * i * rs, pl.tile, dst + (4 * i + pw) * 1024);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16s(qc + 16 * i * rs, pl.tile, slot + kTQ + (4 * i + pw) * 1024);
-    if (pw == 3) {
-#pragma unroll
-      for (int m = 0; m < kDmaV; ++m) dma16s(vc + 32 * m * vrs, pl.v, slot + kTV + m * 1024);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)min(pl.row0 + 16 * i, L - 1) * (uint32_t)rs + 16 * pl.lc;
+        dma16s(base, off, dst + (4 * i + pw) * 1024);
+      }
     }
-  } else {
+  } else if (pw == 3) {
+    const unsigned char *vc = vb + (size_t)t0 * vrs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (uint32_t)min(pl.row0 + 16 * i, L - 1) * (uint32_t)rs + 16 * pl.lc;
-      dma16s(kc, off, slot + kTK + (4 * i + pw) * 1024);
-      dma16s(qc, off, slot + kTQ + (4 * i + pw) * 1024);
-    }
-    if (pw == 3) {
-#pragma unroll
-      for (int m = 0; m < kDmaV; ++m) {
+    for (int m = 0; m < kDmaV; ++m) {
+      if (L == kChunk) {
+        dma16s(vc + 32 * m * vrs, pl.v, slot + kTV + m * 1024);
+      } else {
         const uint32_t off = (uint32_t)min(32 * m + (l >> 1), L - 1) * (uint32_t)vrs + (pl.v % (uint32_t)vrs);
         dma16s(vc, off, slot + kTV + m * 1024);
       }
     }
   }
 }
-
-// Record of chunk slot `slot_idx` into a record ring slot: part A is KiB pw and pw + 4, part B
-// KiB pw + 8, pw + 12 and, below 19, pw + 16 (KiB 18 is half full).
-template <int Part>
-__device__ __forceinline__ void dma_rec(int64_t slot_idx, int h, int Hv, int pw, int l,
-                                        const uint8_t *rec, const ProducerLanes &pl,
-                                        unsigned slot) {
-  const uint8_t *rp = rec + ((size_t)slot_idx * Hv + h) * kRecBytes;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = kProducerWaves * (2 * Part + i) + pw;
-    dma16s(rp + m * 1024, pl.rec, slot + m * 1024);
-  }
-  if (Part == 1 && pw < 3) {
-    const int m = 16 + pw;
-    if (m < kDmaRec - 1 || l < (kRecBytes - (kDmaRec - 1) * 1024) / 16)
-      dma16s(rp + m * 1024, pl.rec, slot + m * 1024);
-  }
+__device__ __forceinline__ void dma_tiles_all(int c, int tb, int te, int Hk, int Hv, int pw, int l,
+                                              const unsigned char *kb, const unsigned char *qb,
+                                              const unsigned char *vb, const uint8_t *tp,
+                                              const ProducerLanes &pl, unsigned slot) {
+  dma_tiles<0>(c, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, slot);
+  dma_tiles<1>(c, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, slot);
+  dma_tiles<2>(c, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, slot);
 }
+
+// The record of a chunk (chunk_prep.hip).  Its T' fragments (12 KiB) travel with the tiles, two
+// chunks ahead.  Its P fragments (6 KiB) are each read by exactly one output wave (row block w's
+// by output wave w), so they go from global memory (L2, warmed by the prefetch wave) straight into
+// that wave's registers with 16-byte loads, 1 KiB contiguous per fragment, issued one chunk ahead
+// right after the previous fragments' last use.  Row block w owns fragments frag_base(w) and, for
+// w >= 2, frag_base(w) + 1; waves 0 and 1 load fragment frag_base(w) twice so that every wave
+// issues the same loads.  The decays (512 B, read by all eight waves) go to a small LDS ring.
+__device__ __forceinline__ const uint8_t *rec_at(const uint8_t *rec, int64_t slot, int h, int Hv) {
+  return rec + ((size_t)slot * Hv + h) * kRecBytes;
+}
+__device__ __forceinline__ int frag_base(int w) { return w < 2 ? w : 2 * w - 2; }
+__device__ __forceinline__ int frag_next(int w) { return w < 2 ? w : 2 * w - 1; }
+
+struct PFrags {
+  bf16x8 p[2];  // P fragments frag_base(w), frag_next(w)
+};
+__device__ __forceinline__ void load_p(PFrags &r, const uint8_t *rp, int w, int l) {
+  r.p[0] = *reinterpret_cast<const bf16x8 *>(rp + kRecP + frag_base(w) * kFragBytes + l * 16);
+  r.p[1] = *reinterpret_cast<const bf16x8 *>(rp + kRecP + frag_next(w) * kFragBytes + l * 16);
+}
+// Decays of chunk slot `slot_idx` into a decay ring slot: lanes 0..31, 16 bytes each.
+__device__ __forceinline__ void dma_dec(int64_t slot_idx, int h, int Hv, int l, const uint8_t *rec,
+                                        unsigned slot) {
+  if (l < kDecBytes / 16) dma16s(rec_at(rec, slot_idx, h, Hv) + kRecEG, 16 * l, slot);
+}
+// Offsets in a decay ring slot.
+constexpr int kDecEG = 0;
+constexpr int kDecED = kRecED - kRecEG;
 
 // L2 warm-up: one 4-byte load per 128-byte line.  The lines that the producers of all
 // workgroups sharing them will load -- the K and Q tiles (shared by the r = Hv / Hk heads of a
@@ -296,17 +321,15 @@ __device__ __forceinline__ f32x4 out_qh(const unsigned char *qt, const unsigned 
                   lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), O);
   return O;
 }
-__device__ __forceinline__ void out_stage(f32x4 O, const unsigned char *rs, const unsigned char *Uo,
-                                          int w, int l, unsigned char *oslot) {
+__device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const unsigned char *ds,
+                                          const unsigned char *Uo, int w, int l,
+                                          unsigned char *oslot) {
   const int lj = l & 15, lg = l >> 4;
-  const f32x4 eg = *reinterpret_cast<const f32x4 *>(rs + kRecEG + (16 * w + 4 * lg) * 4);
+  const f32x4 eg = *reinterpret_cast<const f32x4 *>(ds + kDecEG + (16 * w + 4 * lg) * 4);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) O[rr] *= eg[rr];
-  const int fb = w < 2 ? w : 2 * w - 2;
-  O = mfma_bf16(lds_bf16x8(rs + kRecP + fb * kFragBytes + l * 16), lds_bf16x8(Uo + pmaj(lj, 4 * lg)), O);
-  if (w >= 2)
-    O = mfma_bf16(lds_bf16x8(rs + kRecP + (fb + 1) * kFragBytes + l * 16),
-                  lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)), O);
+  O = mfma_bf16(r.p[0], lds_bf16x8(Uo + pmaj(lj, 4 * lg)), O);
+  if (w >= 2) O = mfma_bf16(r.p[1], lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)), O);
   store_u32x2(oslot + 8 * l, pack_bf16x2(O[0], O[1]), pack_bf16x2(O[2], O[3]));
 }
 
@@ -315,13 +338,12 @@ __device__ __forceinline__ void out_stage(f32x4 O, const unsigned char *rs, cons
 // their output rows are never stored.  The chunk's K, Q and V tiles are in tile ring slot TS,
 // its record in record ring slot RS (compile-time, so that the slot offsets fold into the LDS
 // instructions).  The output path runs on the output waves (out_qh, out_stage).
-template <int TS, int RS>
-__device__ __forceinline__ void chunk_step(const unsigned char *tiles, const unsigned char *recs,
-                                           int w, int l, f32x4 (&H)[2], unsigned char *Ht,
+// One chunk on compute wave w: tile slot ts, decay slot ds.
+__device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *ds, int w,
+                                           int l, f32x4 (&H)[2], unsigned char *Ht,
                                            unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
                                            unsigned char *Ul, unsigned char *Uo) {
   const int lj = l & 15, lg = l >> 4;
-  const unsigned char *ts = tiles + TS * kTileBytes, *rs = recs + RS * kRecBytes;
   const unsigned char *kt = ts + kTK;
 
   // K^T fragments for the state update, read transposed from the K tile: fragment (accumulator
@@ -352,9 +374,9 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
                    lds_bf16x8(Ht + vmaj(lj, 32 * ks + 32 + 8 * lg)), X2);
   }
   X += X2;
-  const f32x4 eg = *reinterpret_cast<const f32x4 *>(rs + kRecEG + (16 * w + 4 * lg) * 4);
-  const f32x4 ed = *reinterpret_cast<const f32x4 *>(rs + kRecED + (16 * w + 4 * lg) * 4);
-  const float egc = *reinterpret_cast<const float *>(rs + kRecEG + 63 * 4);
+  const f32x4 eg = *reinterpret_cast<const f32x4 *>(ds + kDecEG + (16 * w + 4 * lg) * 4);
+  const f32x4 ed = *reinterpret_cast<const f32x4 *>(ds + kDecED + (16 * w + 4 * lg) * 4);
+  const float egc = *reinterpret_cast<const float *>(ds + kDecEG + (kChunk - 1) * 4);
   // V[16 w + 4 lg + rr][lj], rr = 0..3, in one transposing read: lane r of each lane group names
   // row 16 w + 4 lg + r / 4, columns 4 (r % 4) .. + 3 of the row-major V tile.
   float vv[4];
@@ -378,19 +400,17 @@ __device__ __forceinline__ void chunk_step(const unsigned char *tiles, const uns
   __syncthreads();
 
   // U~ = T' R for row block w (3 hi/lo terms; row blocks 2, 3 need two token steps)
-  const int fb = w < 2 ? w : 2 * w - 2;
   f32x4 U = zero4();
   {
-    const bf16x8 th = lds_bf16x8(rs + kRecTpHi + fb * kFragBytes + l * 16);
-    const bf16x8 tl = lds_bf16x8(rs + kRecTpLo + fb * kFragBytes + l * 16);
+    const unsigned char *tt = ts + kTT + frag_base(w) * kFragBytes + l * 16;
+    const bf16x8 th = lds_bf16x8(tt), tl = lds_bf16x8(tt + kTpBytes / 2);
     const bf16x8 bh = lds_bf16x8(Rh + vmaj(lj, 8 * lg));
     const bf16x8 bl = lds_bf16x8(Rl + vmaj(lj, 8 * lg));
     U = mfma_bf16(th, bh, U);
     U = mfma_bf16(th, bl, U);
     U = mfma_bf16(tl, bh, U);
     if (w >= 2) {
-      const bf16x8 th1 = lds_bf16x8(rs + kRecTpHi + (fb + 1) * kFragBytes + l * 16);
-      const bf16x8 tl1 = lds_bf16x8(rs + kRecTpLo + (fb + 1) * kFragBytes + l * 16);
+      const bf16x8 th1 = lds_bf16x8(tt + kFragBytes), tl1 = lds_bf16x8(tt + kFragBytes + kTpBytes / 2);
       const bf16x8 bh1 = lds_bf16x8(Rh + vmaj(lj, 32 + 8 * lg));
       const bf16x8 bl1 = lds_bf16x8(Rl + vmaj(lj, 32 + 8 * lg));
       U = mfma_bf16(th1, bh1, U);
@@ -437,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     unsigned short *__restrict__ o, float *hT,  // hT may equal h0 when h0_index is NULL
     const uint8_t *__restrict__ rec, int Hk, int Hv) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char recs[kRecStages * kRecBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Rh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
@@ -504,13 +524,16 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       unsigned char *oslot = ostage + ow * kOBytes;
       const uint32_t ooff = (uint32_t)(16 * ow + 4 * (l >> 4) + (l & 3)) * (uint32_t)(Hv * kDim * 2) +
                             8 * ((l & 15) >> 2);
+      PFrags pf;
+      load_p(pf, rec_at(rec, slot0, h, Hv), ow, l);
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
         if (c > 0) store_o(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
         const f32x4 O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b1
         __syncthreads();  // b2
-        out_stage(O, recs + (c % kRecStages) * kRecBytes, Uo, ow, l, oslot);
+        out_stage(O, pf, decs + (c % kDecStages) * kDecBytes, Uo, ow, l, oslot);
+        load_p(pf, rec_at(rec, slot0 + min(c + 1, nc - 1), h, Hv), ow, l);
         __syncthreads();  // b3
       }
       store_o(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
@@ -523,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const int pw = w - kComputeWaves;
     if (nc > 0) {
       const unsigned tiles_lds = (unsigned)(uintptr_t)tiles;
-      const unsigned recs_lds = (unsigned)(uintptr_t)recs;
+      const unsigned decs_lds = (unsigned)(uintptr_t)decs;
       const unsigned char *kb = reinterpret_cast<const unsigned char *>(k + (size_t)hk * kDim);
       const unsigned char *qb = reinterpret_cast<const unsigned char *>(q + (size_t)hk * kDim);
       const unsigned char *vb = reinterpret_cast<const unsigned char *>(v + (size_t)h * kDim);
@@ -532,32 +555,35 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       pl.lc = (l & 15) ^ (pl.row0 & 15);
       pl.tile = (uint32_t)pl.row0 * (uint32_t)(Hk * kDim * 2) + 16 * pl.lc;
       pl.v = (uint32_t)(l >> 1) * (uint32_t)(Hv * kDim * 2) + 2 * (d0 + 8 * (l & 1));
-      pl.rec = 16 * l;
       const int c1 = min(1, nc - 1);
-      dma_tiles(0, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl, tiles_lds);
-      dma_rec<0>(slot0, h, Hv, pw, l, rec, pl, recs_lds);
-      dma_rec<1>(slot0, h, Hv, pw, l, rec, pl, recs_lds);
-      dma_tiles(c1, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl, tiles_lds + kTileBytes);
-      dma_rec<0>(slot0 + c1, h, Hv, pw, l, rec, pl, recs_lds + kRecBytes);
-      dma_rec<1>(slot0 + c1, h, Hv, pw, l, rec, pl, recs_lds + kRecBytes);
+      dma_tiles_all(0, tb, te, Hk, Hv, pw, l, kb, qb, vb, rec_at(rec, slot0, h, Hv), pl, tiles_lds);
+      if (pw == kDecWave) dma_dec(slot0, h, Hv, l, rec, decs_lds);
+      dma_tiles_all(c1, tb, te, Hk, Hv, pw, l, kb, qb, vb, rec_at(rec, slot0 + c1, h, Hv), pl,
+                    tiles_lds + kTileBytes);
+      if (pw == kDecWave) dma_dec(slot0 + c1, h, Hv, l, rec, decs_lds + kDecBytes);
       // chunk 0 has landed: only chunk 1's loads may still be in flight
-      if (pw == 3) wait_vmcnt<kChunkCount(3)>(); else wait_vmcnt<kChunkCount(0)>();
+      if (pw == 3) wait_vmcnt<kChunkCount(3)>();
+      else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
+      else wait_vmcnt<kChunkCount(0)>();
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
-        // Chunk c + 2 is loaded during chunk c (clamped reloads of the last chunk only go to
-        // slots that are no longer read).  Its record slot (c + 2) % 3 held chunk c - 1, done
-        // before the last barrier; its tile slot c % 2 holds chunk c's tiles, done after b1.
+        // Chunk c + 2 is loaded during chunk c, spread over its three phases, into tile and decay
+        // slots (c + 2) % 3, which held chunk c - 1 (clamped reloads of the last chunk only go to
+        // slots that are no longer read): K before b1, Q before b2, V and the decays before b3.
         const int cn = min(c + 2, nc - 1);
-        const unsigned rslot = recs_lds + ((c + 2) % kRecStages) * kRecBytes;
-        dma_rec<0>(slot0 + cn, h, Hv, pw, l, rec, pl, rslot);
+        const unsigned tslot = tiles_lds + ((c + 2) % kTileStages) * kTileBytes;
+        const uint8_t *tp = rec_at(rec, slot0 + cn, h, Hv);
+        dma_tiles<0>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
         __syncthreads();  // b1
-        dma_tiles(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, pl,
-                  tiles_lds + (c % kTileStages) * kTileBytes);
+        dma_tiles<1>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
         __syncthreads();  // b2
-        dma_rec<1>(slot0 + cn, h, Hv, pw, l, rec, pl, rslot);
+        dma_tiles<2>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
+        if (pw == kDecWave) dma_dec(slot0 + cn, h, Hv, l, rec, decs_lds + ((c + 2) % kDecStages) * kDecBytes);
         // Chunk c + 1 (loaded during chunk c - 1) must have landed before b3: loads complete in
         // issue order, so it is enough that at most this iteration's loads are in flight.
-        if (pw != 3) wait_vmcnt<kChunkCount(0)>(); else wait_vmcnt<kChunkCount(3)>();
+        if (pw == 3) wait_vmcnt<kChunkCount(3)>();
+        else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
+        else wait_vmcnt<kChunkCount(0)>();
         __syncthreads();  // b3
       }
     }
@@ -587,22 +613,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
                   pack_bf16x2(H[a][2], H[a][3]));
     __syncthreads();
-    // six chunks per trip, so that every chunk's ring slots (c % 2, c % 3) are compile-time
-#define GDN_STEP(ts, rs) chunk_step<ts, rs>(tiles, recs, w, l, H, Ht, Rh, Rl, Uh, Ul, Uo)
-    for (int c = 0; c < nc; c += 6) {
-      GDN_STEP(0, 0);
-      if (c + 1 == nc) break;
-      GDN_STEP(1, 1);
-      if (c + 2 == nc) break;
-      GDN_STEP(0, 2);
-      if (c + 3 == nc) break;
-      GDN_STEP(1, 0);
-      if (c + 4 == nc) break;
-      GDN_STEP(0, 1);
-      if (c + 5 == nc) break;
-      GDN_STEP(1, 2);
-    }
-#undef GDN_STEP
+    for (int c = 0; c < nc; ++c)
+      chunk_step(tiles + (c % kTileStages) * kTileBytes, decs + (c % kDecStages) * kDecBytes, w, l, H,
+                 Ht, Rh, Rl, Uh, Ul, Uo);
   }
 
   if (hT) {
