@@ -146,8 +146,8 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
     Gall[kChunk * hh + l] = G;
     Ball[kChunk * hh + l] = bv;
     uint8_t *R = rec_slot + (size_t)h * kRecBytes;
-    reinterpret_cast<float *>(R + kRecEG)[l] = exp_neg(G);
-    reinterpret_cast<float *>(R + kRecED)[l] = exp_neg(Glast - G);
+    __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
+    __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
   }
   __syncthreads();
 
@@ -205,9 +205,9 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
                          frag_index(rb, cb >> 1) * kFragBytes + l * 16 + 8 * (cb & 1);
           if ((cb & 1) == 0 && cb + 1 > rb) {  // the other half is an upper block: zeros
             const u32x4 v4 = {val[0], val[1], 0u, 0u};
-            *reinterpret_cast<u32x4 *>(dst) = v4;
+            __builtin_nontemporal_store(v4, reinterpret_cast<u32x4 *>(dst));
           } else {
-            *reinterpret_cast<u32x2 *>(dst) = val;
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x2 *>(dst));
           }
         } else {
           float *Ax = reinterpret_cast<float *>(smem + kOffA + x * kMatBytes);
@@ -318,8 +318,8 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) split_pair(t[2 * e], t[2 * e + 1], hv[e], lv[e]);
     const u32x4 vh = {hv[0], hv[1], hv[2], hv[3]}, vl = {lv[0], lv[1], lv[2], lv[3]};
-    *reinterpret_cast<u32x4 *>(R + kRecTpHi + f * kFragBytes + ll * 16) = vh;
-    *reinterpret_cast<u32x4 *>(R + kRecTpLo + f * kFragBytes + ll * 16) = vl;
+    __builtin_nontemporal_store(vh, reinterpret_cast<u32x4 *>(R + kRecTpHi + f * kFragBytes + ll * 16));
+    __builtin_nontemporal_store(vl, reinterpret_cast<u32x4 *>(R + kRecTpLo + f * kFragBytes + ll * 16));
   }
 }
 

@@ -14,7 +14,7 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
                        void *rec, hipStream_t stream);
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
-                       const void *rec, int N, int Hk, int Hv, hipStream_t stream);
+                       const void *rec, int64_t T, int N, int Hk, int Hv, hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, const void *conv_in, const int32_t *state_index,
                        int num_states, void *q, void *k, void *v, hipStream_t stream);
@@ -159,8 +159,8 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
     if (e != hipSuccess) return record_hip(e);
   }
   if (stage & kPass) {
-    gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.N, s.Hk,
-                           s.Hv, stream);
+    gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T, s.N,
+                           s.Hk, s.Hv, stream);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;

@@ -52,6 +52,7 @@ constexpr int kOutputWave0 = kComputeWaves + kProducerWaves;
 constexpr int kPrefetchWave = kOutputWave0 + kOutputWaves;
 constexpr int kThreads = 64 * (kPrefetchWave + 1);
 constexpr int kPrefetchAhead = 6;     // chunks between the L2 warm-up of a chunk and its use
+constexpr uint64_t kOStreamBytes = 16u << 20;  // o up to this size: streaming stores (store_o)
 // Tile ring slot: K tile | Q tile (64 x 128 bf16 each, swizzled) | V tile (64 x 16 bf16) |
 // T' hi and lo fragments of the record (12 KiB, as stored).
 constexpr int kTileStages = 3;
@@ -292,6 +293,11 @@ __device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, in
 // lane i of lane group g row 4 g + i % 4, columns 4 (i / 4) .. + 3: lane r of the group names
 // column 4 (r % 4) + r / 4, rows 4 g .. 4 g + 3 (see lds_read_tr16).  ob points at column d0 of
 // this head in row 0 (bytes); ooff = row * Hv * 256 + 8 (i / 4) is the lane's fixed offset.
+// nt: streaming (non-temporal) stores, chosen by the host when all of o fits in L2 -- then the
+// dirty o lines would otherwise be written back at the kernel's end, after the last chunk; a
+// larger o is mostly evicted during the kernel anyway, and its 32-byte column slices merge into
+// whole lines in L2 first.
+template <bool kNt>
 __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, int l,
                                         const unsigned char *slot, unsigned char *ob, uint32_t ooff) {
   const int g = l >> 4, i = l & 15;
@@ -300,7 +306,9 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
   const int t0 = tb + kChunk * c;
   if (16 * pw + 4 * g + (i & 3) < min(kChunk, te - t0)) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2 *>(ob + (size_t)t0 * Hv * kDim * 2 + ooff) = __builtin_bit_cast(u32x2, val);
+    u32x2 *dst = reinterpret_cast<u32x2 *>(ob + (size_t)t0 * Hv * kDim * 2 + ooff);
+    if (kNt) __builtin_nontemporal_store(__builtin_bit_cast(u32x2, val), dst);
+    else *dst = __builtin_bit_cast(u32x2, val);
   }
 }
 
@@ -450,6 +458,7 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
 
 }  // namespace
 
+template <bool kONt>
 __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       load_p(pf, rec_at(rec, slot0, h, Hv), ow, l);
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
-        if (c > 0) store_o(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+        if (c > 0) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
         const f32x4 O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b1
         __syncthreads();  // b2
@@ -536,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         load_p(pf, rec_at(rec, slot0 + min(c + 1, nc - 1), h, Hv), ow, l);
         __syncthreads();  // b3
       }
-      store_o(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+      store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
     }
     return;
   }
@@ -624,16 +633,18 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int key = state_key(w, a, 4 * lg + rr);
-        hT[state_base + (size_t)key * kDim + d0 + lj] = H[a][rr];
+        __builtin_nontemporal_store(H[a][rr], hT + state_base + (size_t)key * kDim + d0 + lj);
       }
   }
 }
 
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
-                       const void *rec, int N, int Hk, int Hv, hipStream_t stream) {
+                       const void *rec, int64_t T, int N, int Hk, int Hv, hipStream_t stream) {
   const unsigned nblocks = (unsigned)N * (unsigned)Hv * kDvTiles;
-  hipLaunchKernelGGL(state_pass_kernel, dim3(nblocks), dim3(kThreads), 0, stream,
+  const bool o_nt = (uint64_t)T * (uint64_t)Hv * kDim * 2 <= kOStreamBytes;
+  hipLaunchKernelGGL(o_nt ? state_pass_kernel<true> : state_pass_kernel<false>, dim3(nblocks),
+                     dim3(kThreads), 0, stream,
                      static_cast<const unsigned short *>(q), static_cast<const unsigned short *>(k),
                      static_cast<const unsigned short *>(v), cu, h0, h0_index, num_h0,
                      static_cast<unsigned short *>(o), hT, static_cast<const uint8_t *>(rec), Hk, Hv);
