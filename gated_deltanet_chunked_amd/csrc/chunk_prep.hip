@@ -20,6 +20,9 @@
 //      the column's blocks kept in registers, one wave per block column (no barrier in between).
 //   5. T' = T diag(beta) as bf16 hi + lo MFMA fragments, e^{G} and e^{G_last - G}: the rest of the
 //      record the state pass reads.
+// The record is written with streaming (non-temporal) stores: only the next kernel reads it, often
+// from another XCD, so it should be in memory when this kernel ends rather than written back from
+// L2 at the kernel boundary.
 // Every exponent is <= 0 (G is non-increasing), so no e^{-G} is ever formed.  Tokens past the
 // end of a sequence enter as k = q = 0, g = 0, beta = 0, which leaves T' and P zero on them.
 #include "gdn_device.h"

@@ -17,26 +17,27 @@
 // The hi/lo splits keep the state path at about 16 significant bits per operand, so the fp32
 // state does not drift over hundreds of chunks; bf16 is used where only the output sees it.
 //
-// A chunk takes three phases on the compute waves, separated by workgroup barriers b1, b2, b3:
-//   phase 1: K^T fragments, X and Q H from the K/Q/V tiles; R to LDS            -> b1
-//   phase 2: U~ = T' R; U~ (decayed hi/lo and plain) to LDS                      -> b2
-//   phase 3: o = e^G o (Q H) + P U~ to an LDS staging slot; H update; bf16 H     -> b3
-// Data movement (four producer waves + four compute waves per workgroup, one of each per SIMD):
-//   * The producer waves do all of the global loads, with global->LDS loads
-//     (global_load_lds_dwordx4: 1 KiB per instruction, no VGPRs).  The K, Q and V tiles are only
-//     read in phase 1, so their 2-deep ring slot is refilled with the tiles of chunk c + 2 right
-//     after b1 of chunk c; the record (T' hi/lo, P, decays), read until phase 3, has a 3-deep
-//     ring refilled two chunks ahead.  Every load thus has well over a chunk to land, from L2:
-//     a ninth wave pulls every line into L2 six chunks ahead of use, with loads it never waits
-//     for, since a miss to HBM takes longer than a chunk.  The producers also write the output
-//     rows that the compute waves leave in LDS.
-//   * Each producer wave's loads are a fixed share, spread over the barrier intervals: a CU's
-//     vector memory unit moves well under 64 B per clock, so a wave issuing a whole chunk at once
-//     stalls (and holds up the next barrier), and a compute wave touching global memory would
-//     wait behind the producers' queue.  The compute waves do no global access in the chunk loop.
-//   * The compute waves read every operand from LDS (K^T fragments come from the K tile through
-//     transposing LDS reads); LDS also carries the three cross-wave exchanges per chunk: bf16 H,
-//     R and U~.
+// A chunk takes three phases, separated by workgroup barriers b1, b2, b3:
+//   phase 1: compute waves: K^T fragments, X = K H, R = V - e^G o X to LDS (hi/lo)
+//            output waves:  Q H                                                     -> b1
+//   phase 2: compute waves: U~ = T' R; U~ (decayed hi/lo and plain) to LDS           -> b2
+//   phase 3: compute waves: H update, bf16 H to LDS
+//            output waves:  o = e^G o (Q H) + P U~ into an LDS staging slot           -> b3
+// and the output waves store chunk c's rows at the start of chunk c + 1.
+// Thirteen waves per workgroup:
+//   * 4 compute waves (one per SIMD) keep the state and do no global access in the chunk loop.
+//   * 4 producer waves issue the bulk loads as global->LDS loads (global_load_lds_dwordx4: 1 KiB
+//     per instruction, no VGPRs) into a 3-deep ring: the K, Q and V tiles and the record's T'
+//     fragments of chunk c + 2 go into the slot chunk c - 1 left, spread over the three phases
+//     of chunk c (K before b1, Q before b2, V, the last third of T' and the decays before b3), so
+//     no phase waits on a burst of load issue.  Each wave's share is fixed, so the vmcnt
+//     bookkeeping is static.
+//   * 4 output waves (one per row block) compute the output; each loads its own P fragments
+//     straight into registers a chunk ahead and issues no global->LDS loads, so its LDS reads
+//     never queue behind its own loads.
+//   * 1 prefetch wave pulls every line into L2 six chunks ahead of use, with loads it never waits
+//     for, since a miss to HBM takes longer than a chunk.
+// LDS carries the tiles and the three cross-wave exchanges per chunk: bf16 H, R and U~.
 #include "gdn_device.h"
 
 namespace gdn {
@@ -315,8 +316,9 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
 // The output path o = e^G o (Q H) + P U~ for row block w of a chunk, on the output wave that
 // shares a SIMD with compute wave w.  It issues no global->LDS loads: a wave's LDS reads wait for
 // its own global->LDS loads still in flight, which would tie these reads to load latency.  out_qh
-// runs before b1: Q H needs the chunk's entry state, which the compute waves overwrite in phase 3,
-// and the Q tile, whose ring slot the producers refill after b1.  out_stage runs after b2, once U~
+// runs before b1: Q H needs the chunk's entry state, which the compute waves overwrite in phase 3
+// (b1 is the natural point; the Q tile's slot is not refilled before chunk c + 1).  out_stage runs
+// after b2, once U~
 // is in LDS: it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg ..
 // + 3 of column lj at byte 8 l); they are read back transposed and stored at the start of the
 // next chunk (store_o).
@@ -341,12 +343,10 @@ __device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const unsign
   store_u32x2(oslot + 8 * l, pack_bf16x2(O[0], O[1]), pack_bf16x2(O[2], O[3]));
 }
 
-// One chunk on the compute waves.  Rows past the sequence end hold clamped data; they need no
-// masking because T' has zero rows and columns there (beta = 0), so U~ is zero on them, and
-// their output rows are never stored.  The chunk's K, Q and V tiles are in tile ring slot TS,
-// its record in record ring slot RS (compile-time, so that the slot offsets fold into the LDS
-// instructions).  The output path runs on the output waves (out_qh, out_stage).
-// One chunk on compute wave w: tile slot ts, decay slot ds.
+// One chunk on compute wave w: tile ring slot ts (K, Q, V tiles and T' fragments), decay ring
+// slot ds.  Rows past the sequence end hold clamped data; they need no masking because T' has
+// zero rows and columns there (beta = 0), so U~ is zero on them, and their output rows are never
+// stored.  The output path runs on the output waves (out_qh, out_stage).
 __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *ds, int w,
                                            int l, f32x4 (&H)[2], unsigned char *Ht,
                                            unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
