@@ -102,8 +102,17 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   float *Gall = reinterpret_cast<float *>(smem + kOffG);
   float *Ball = reinterpret_cast<float *>(smem + kOffB);
 
-  const int slot = blockIdx.x;
-  const int h_first = blockIdx.y * HP, hk = h_first / (Hv / Hk);
+  // Workgroup b runs on XCD b % 8.  For one sequence the state pass keeps v-heads
+  // [x Hv / 8, (x + 1) Hv / 8) on XCD x; dealing the (slot, head group) units out the same way puts
+  // each head's prep on the XCD (and L2) that reads its q and k next.
+  int slot = blockIdx.x, grp = blockIdx.y;
+  if (N == 1 && gridDim.y % 8 == 0) {
+    const int nb = gridDim.x * gridDim.y, bid = blockIdx.y * gridDim.x + blockIdx.x;
+    const int lid = (bid % 8) * (nb / 8) + bid / 8;
+    slot = lid % gridDim.x;
+    grp = lid / gridDim.x;
+  }
+  const int h_first = grp * HP, hk = h_first / (Hv / Hk);
   const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = w >> 2, wl = w & 3;  // this wave's v-head within the group, wave within the head
