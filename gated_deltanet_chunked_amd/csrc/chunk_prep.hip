@@ -15,8 +15,8 @@
 //   3. From the accumulators, per v-head:
 //        A_ij = beta_i e^{G_i - G_j} (k_i . k_j)  for i > j      (fp32, LDS)
 //        P_ij = e^{G_i - G_j} (q_i . k_j)         for i >= j     (bf16, straight to the record)
-//   4. T = (I + A)^-1: each 16x16 diagonal block by right-looking substitution (one column per
-//      lane), then block column j by T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, with
+//   4. T = (I + A)^-1: each 16x16 diagonal block by right-looking substitution (four lanes per
+//      column), then block column j by T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, with
 //      the column's blocks kept in registers, one wave per block column (no barrier in between).
 //   5. T' = T diag(beta) as bf16 hi + lo MFMA fragments, e^{G} and e^{G_last - G}: the rest of the
 //      record the state pass reads.
@@ -48,6 +48,18 @@ static_assert(kMaxHeads * kMatBytes >= 2 * kChunk * kDim * 2, "the A matrices co
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The value of lane 4 (l / 4) + q (lane q of this lane's quad), through a DPP quad permutation;
+// q must fold to a constant (the DPP control is an immediate).
+__device__ __forceinline__ float quad_bcast(float v, int q) {
+  const int b = __float_as_int(v);
+  switch (q) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xFF, 0xF, 0xF, false));
+  }
+}
 
 // Byte offset of bf16 element (row, col) in a swizzled 64 x 128 tile: 16-byte chunks are
 // XOR-permuted by row so that 16 lanes reading one chunk column of 16 rows hit distinct banks.
@@ -244,65 +256,86 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   // ---- 4. T = (I + A)^-1 for this wave's v-head ------------------------------------------------
   const float *As = reinterpret_cast<const float *>(smem + kOffA + hh * kMatBytes);
   float *Ts = reinterpret_cast<float *>(smem + kOffT + hh * kMatBytes);
-  // Diagonal block wl, column cj = lane: right-looking substitution (each step waits for one
-  // multiply-add of the previous one).  Step m needs column m of the block below the diagonal,
-  // which the transposed storage makes a contiguous row.
-  if (l < 16) {
-    const int cj = l, o = 16 * wl;
-    float x[16];
+  // Diagonal block wl by right-looking substitution on all 64 lanes: lane 4 cj + r holds rows
+  // 4 r .. 4 r + 3 of column cj of the block's inverse.  Step m broadcasts x_m (row m, held by
+  // lane 4 cj + m / 4) across the lane quad and subtracts A[i][m] x_m from every row i; A[i][m]
+  // is 0 for i <= m (A is strictly lower), so no row needs masking.  The 15 columns of A that the
+  // steps use sit contiguously in the transposed diagonal-block storage and are read up front.
+  {
+    const int o = 16 * wl, cj = l >> 2, r = l & 3;
+    f32x4 ac[15];  // ac[m][e] = A[o + 4 r + e][o + m]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = i == cj ? 1.f : 0.f;
+    for (int m = 0; m < 15; ++m) ac[m] = *reinterpret_cast<const f32x4 *>(As + (o + m) * kPitchF + o + 4 * r);
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = 4 * r + e == cj ? 1.f : 0.f;
 #pragma unroll
     for (int m = 0; m < 15; ++m) {
-      float a[16];
+      const float xm = quad_bcast(x[m % 4], m / 4);
 #pragma unroll
-      for (int v4 = (m + 1) / 4; v4 < 4; ++v4) {
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(As + (o + m) * kPitchF + o + 4 * v4);
-        a[4 * v4] = t[0], a[4 * v4 + 1] = t[1], a[4 * v4 + 2] = t[2], a[4 * v4 + 3] = t[3];
-      }
-#pragma unroll
-      for (int i = m + 1; i < 16; ++i) x[i] -= a[i] * x[m];
+      for (int e = 0; e < 4; ++e) x[e] -= ac[m][e] * xm;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Ts[(o + i) * kPitchF + o + cj] = x[i];
+    for (int e = 0; e < 4; ++e) Ts[(o + 4 * r + e) * kPitchF + o + cj] = x[e];
   }
   __syncthreads();
 
-  // Block column j = wl: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj for i = j + 1 .. 3, with the
-  // column's blocks in registers (C layout: lane (col lj, rows 4 lg + rr)).  In every product the
-  // k-slot (step s, lane group lg) stands for row 4 lg + s of the B operand, so an accumulator is
-  // fed back as B without moving data between lanes.
+  // Block column j = wl: T_ij = -T_ii S_i, S_i = sum_{m=j}^{i-1} A_im T_mj for i = j + 1 .. 3.
+  // Every S_i starts with its T_jj term (independent of the chain); each new T_ij is then folded
+  // into the S of the rows below it at once, so the dependent chain is one product by T_ii and one
+  // by A per block.  All operands are read from LDS before the chain starts and the results are
+  // stored after it, so no LDS access waits inside the chain.  The column's blocks stay in
+  // registers (C layout: lane (col lj, rows 4 lg + rr)); in every product the k-slot (step s,
+  // lane group lg) stands for row 4 lg + s of the B operand, so an accumulator is fed back as B
+  // without moving data between lanes.
   {
     const int j = wl;
-    f32x4 Tcol[4];  // Tcol[m] = T_mj for j < m < i
+    // A operands (row lj, cols 4 lg + s): Aj[i] = A_ij, Am[i][m] = A_im (j < m < i), Tii[i] = T_ii;
+    // every register array index is a compile-time constant (j is not).
+    f32x4 Aj[4], Am[4][4], Tii[4], Tjj;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Tjj[s] = Ts[(16 * j + 4 * lg + s) * kPitchF + 16 * j + lj];
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
       if (i > j) {
-        f32x4 S = zero4();
+        Tii[i] = *reinterpret_cast<const f32x4 *>(Ts + (16 * i + lj) * kPitchF + 16 * i + 4 * lg);
+        Aj[i] = *reinterpret_cast<const f32x4 *>(As + (16 * i + lj) * kPitchF + 16 * j + 4 * lg);
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-          if (m >= j && m < i) {
+        for (int m = 1; m < 3; ++m)
+          if (m > j && m < i)
+            Am[i][m] = *reinterpret_cast<const f32x4 *>(As + (16 * i + lj) * kPitchF + 16 * m + 4 * lg);
+      }
+    }
+    f32x4 S[4], Tc[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const float a = As[(16 * i + lj) * kPitchF + 16 * m + 4 * lg + s];
-              const float bb = m == j ? Ts[(16 * m + 4 * lg + s) * kPitchF + 16 * j + lj] : Tcol[m][s];
-              S = mfma_f32(a, bb, S);
-            }
-          }
-        }
+    for (int i = 1; i < 4; ++i) {
+      S[i] = zero4();
+      if (i > j) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) S[i] = mfma_f32(Aj[i][s], Tjj[s], S[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      if (i > j) {
         f32x4 Tb = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float a = Ts[(16 * i + lj) * kPitchF + 16 * i + 4 * lg + s];
-          Tb = mfma_f32(a, S[s], Tb);
-        }
+        for (int s = 0; s < 4; ++s) Tb = mfma_f32(Tii[i][s], S[i][s], Tb);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          Tcol[i][s] = -Tb[s];
-          Ts[(16 * i + 4 * lg + s) * kPitchF + 16 * j + lj] = -Tb[s];
+        for (int s = 0; s < 4; ++s) Tc[i][s] = -Tb[s];
+#pragma unroll
+        for (int i2 = i + 1; i2 < 4; ++i2) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) S[i2] = mfma_f32(Am[i2][i][s], Tc[i][s], S[i2]);
         }
       }
     }
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (i > j) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Ts[(16 * i + 4 * lg + s) * kPitchF + 16 * j + lj] = Tc[i][s];
+      }
   }
   __syncthreads();
 
