@@ -2,6 +2,7 @@
 // Everything is validated before the first enqueue; nothing here allocates, frees or syncs.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -14,7 +15,8 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
                        void *rec, hipStream_t stream);
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
-                       const void *rec, int64_t T, int N, int Hk, int Hv, hipStream_t stream);
+                       const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
+                       hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, const void *conv_in, const int32_t *state_index,
                        int num_states, void *q, void *k, void *v, hipStream_t stream);
@@ -28,6 +30,25 @@ void launch_gated_rmsnorm(const void *o, const void *z, const void *norm_w, floa
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Workgroups of the state pass that fit on the current device at once (one per CU: its LDS use
+// allows no more), rounded down to a multiple of 8; cached per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_max_groups[kMaxDevices];
+int device_max_groups() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int cached = g_max_groups[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess)
+    cus = 0;
+  const int groups = cus >= 8 ? cus / 8 * 8 : 8;
+  if (dev >= 0) g_max_groups[dev].store(groups, std::memory_order_relaxed);
+  return groups;
+}
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -160,7 +181,7 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
   }
   if (stage & kPass) {
     gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T, s.N,
-                           s.Hk, s.Hv, stream);
+                           s.Hk, s.Hv, device_max_groups(), stream);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;

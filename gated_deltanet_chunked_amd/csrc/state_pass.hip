@@ -346,7 +346,10 @@ __device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const unsign
 // One chunk on compute wave w: tile ring slot ts (K, Q, V tiles and T' fragments), decay ring
 // slot ds.  Rows past the sequence end hold clamped data; they need no masking because T' has
 // zero rows and columns there (beta = 0), so U~ is zero on them, and their output rows are never
-// stored.  The output path runs on the output waves (out_qh, out_stage).
+// stored.  The output path runs on the output waves (out_qh, out_stage).  With kWriteHt the step
+// ends with the bf16 copy of the new state in the exchange buffer and the chunk's last barrier (b3);
+// without it the caller does both, after any change of H between items.
+template <bool kWriteHt>
 __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *ds, int w,
                                            int l, f32x4 (&H)[2], unsigned char *Ht,
                                            unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
@@ -449,15 +452,145 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
       H[a] = mfma_bf16(kc[a][ks], bl, H[a]);
     }
   }
+  if constexpr (kWriteHt) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+      store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
+                  pack_bf16x2(H[a][2], H[a][3]));
+    __syncthreads();  // b3
+  }
+}
+
+// bf16 copy of this wave's state slice into the H exchange buffer (the B operand of X = K H and
+// Q H in the next chunk).
+__device__ __forceinline__ void write_ht(unsigned char *Ht, const f32x4 (&H)[2], int w, int l) {
+  const int lj = l & 15, lg = l >> 4;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
     store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
                 pack_bf16x2(H[a][2], H[a][3]));
-  __syncthreads();
+}
+
+// ---- Work items --------------------------------------------------------------------------------
+// An item is (sequence n, v-head h, 16-column tile).  The grid has G <= one workgroup per CU
+// (G a multiple of 8); workgroup b takes the items of rounds k = 0, 1, ...: item
+// lid = k G + (b % 8) (G / 8) + b / 8, as long as lid < N Hv 8.  Workgroup b runs on XCD b % 8,
+// so within a round each XCD holds a contiguous range of items -- the 16 workgroups of a k-head
+// (two v-heads x 8 tiles) share an L2 -- and a workgroup keeps one tile in every round.  A
+// workgroup walks the chunks of its items as one stream of steps, so the loads of the next item
+// overlap the last chunks of the current one.
+struct Item {
+  int n, h, hk, tb, te, nc;
+  int64_t slot0;  // record slot of chunk 0: tb / 64 + n
+};
+struct Walker {
+  int k, c;  // item round, chunk within the item
+  Item it;
+  bool valid;
+};
+struct Grid {
+  int G, total, Hv, r;  // r = Hv / Hk
+};
+__device__ __forceinline__ bool item_at(const Grid &g, int k, const int32_t *cu, Item &it) {
+  const int b = blockIdx.x;
+  const int64_t lid = (int64_t)k * g.G + (b % 8) * (g.G / 8) + b / 8;
+  if (lid >= g.total) return false;
+  const int rest = (int)(lid / kDvTiles);
+  it.h = rest % g.Hv;
+  it.n = rest / g.Hv;
+  it.hk = it.h / g.r;
+  it.tb = cu[it.n];
+  it.te = cu[it.n + 1];
+  it.nc = (it.te - it.tb + kChunk - 1) / kChunk;
+  it.slot0 = it.tb / kChunk + it.n;
+  return true;
+}
+// The next item with at least one chunk after round W.k; W.valid = false past the last.
+__device__ __forceinline__ void next_item(Walker &W, const Grid &g, const int32_t *cu) {
+  for (;;) {
+    ++W.k;
+    if (!item_at(g, W.k, cu, W.it)) {
+      W.valid = false;
+      return;
+    }
+    if (W.it.nc > 0) {
+      W.c = 0;
+      W.valid = true;
+      return;
+    }
+  }
+}
+__device__ __forceinline__ Walker first_step(const Grid &g, const int32_t *cu) {
+  Walker W;
+  W.k = -1;
+  next_item(W, g, cu);
+  return W;
+}
+__device__ __forceinline__ void next_step(Walker &W, const Grid &g, const int32_t *cu) {
+  if (++W.c == W.it.nc) next_item(W, g, cu);
+}
+// Look-ahead for loads: past the last step it stays on the last step (a reload into a slot that is
+// no longer read), so that every step issues the same loads.
+__device__ __forceinline__ void next_step_clamped(Walker &W, const Grid &g, const int32_t *cu) {
+  Walker t = W;
+  next_step(t, g, cu);
+  if (t.valid) W = t;
+}
+
+// Initial state slice of item it for compute wave w (H[a][rr] = state row state_key(w, a,
+// 4 lg + rr), column d0 + lj): h0[h0_index[n]] of the pool, zeros outside [0, num_h0), h0[n]
+// without an index, zeros without h0.
+__device__ __forceinline__ void load_h0(f32x4 (&H)[2], const Item &it, const float *h0,
+                                        const int32_t *h0_index, int num_h0, int Hv, int d0,
+                                        int w, int l) {
+  const float *h0s = nullptr;
+  if (h0) {
+    const int r = h0_index ? h0_index[it.n] : it.n;
+    if (r >= 0 && r < num_h0) h0s = h0 + ((size_t)r * Hv + it.h) * kDim * kDim;
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int key = state_key(w, a, 4 * (l >> 4) + rr);
+      H[a][rr] = h0s ? h0s[(size_t)key * kDim + d0 + (l & 15)] : 0.f;
+    }
+}
+__device__ __forceinline__ void store_ht(const f32x4 (&H)[2], const Item &it, float *hT, int Hv,
+                                         int d0, int w, int l) {
+  if (!hT) return;
+  float *dst = hT + ((size_t)it.n * Hv + it.h) * kDim * kDim + d0 + (l & 15);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      __builtin_nontemporal_store(H[a][rr], dst + (size_t)state_key(w, a, 4 * (l >> 4) + rr) * kDim);
+}
+// The compute waves' walk to the next non-empty item: an empty sequence's final state is its
+// initial state, copied here.
+__device__ __forceinline__ void next_item_copying(Walker &W, const Grid &g, const int32_t *cu,
+                                                  const float *h0, const int32_t *h0_index,
+                                                  int num_h0, float *hT, int d0, int w, int l) {
+  for (;;) {
+    ++W.k;
+    if (!item_at(g, W.k, cu, W.it)) {
+      W.valid = false;
+      return;
+    }
+    if (W.it.nc > 0) {
+      W.c = 0;
+      W.valid = true;
+      return;
+    }
+    f32x4 Hc[2];
+    load_h0(Hc, W.it, h0, h0_index, num_h0, g.Hv, d0, w, l);
+    store_ht(Hc, W.it, hT, g.Hv, d0, w, l);
+  }
 }
 
 }  // namespace
 
+// One item per workgroup (launches whose items all fit on the device at once).
 template <bool kONt>
 __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
@@ -623,8 +756,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
                   pack_bf16x2(H[a][2], H[a][3]));
     __syncthreads();
     for (int c = 0; c < nc; ++c)
-      chunk_step(tiles + (c % kTileStages) * kTileBytes, decs + (c % kDecStages) * kDecBytes, w, l, H,
-                 Ht, Rh, Rl, Uh, Ul, Uo);
+      chunk_step<true>(tiles + (c % kTileStages) * kTileBytes, decs + (c % kDecStages) * kDecBytes, w,
+                       l, H, Ht, Rh, Rl, Uh, Ul, Uo);
   }
 
   if (hT) {
@@ -638,16 +771,220 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   }
 }
 
+// Persistent workgroups walking several items each (launches with more items than fit at once).
+template <bool kONt>
+__global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
+    const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
+    const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
+    const float *h0, const int32_t *__restrict__ h0_index, int num_h0,
+    unsigned short *__restrict__ o, float *hT,  // hT may equal h0 when h0_index is NULL
+    const uint8_t *__restrict__ rec, int Hk, int Hv, int total_items) {
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Rh[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Uh[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Ul[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
+  __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
+
+  const Grid gr{(int)gridDim.x, total_items, Hv, Hv / Hk};
+  const int tile = (int)(((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) % kDvTiles);  // every round
+  const int d0 = kDvTile * tile;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int r = Hv / Hk;
+
+  if (w == kPrefetchWave) {
+    // Prefetch wave: warms L2 kPrefetchAhead steps ahead of use and never waits for its loads
+    // inside the loop (so a slow line holds up nothing).  Barriers as the compute waves.  A
+    // sequence's partial last chunk is not warmed (its rows past the end must not be read).
+    Walker cur = first_step(gr, cu);
+    if (cur.valid) {
+      const unsigned sink = (unsigned)(uintptr_t)touch_sink;
+      Walker pf = cur;  // the step warmed next: steps 2 .. kPrefetchAhead - 1 first
+      next_step(pf, gr, cu);
+      if (pf.valid) next_step(pf, gr, cu);
+      __syncthreads();
+      PrefetchLane pl;  // lines of chunk 0 of item round pl_k
+      int pl_k = -1;
+      for (int s = 0; cur.valid; ++s) {
+        for (int cnt = s == 0 ? kPrefetchAhead - 2 : 1; cnt > 0 && pf.valid; --cnt) {
+          const Item &it = pf.it;
+          if (pf.c < (it.te - it.tb) / kChunk) {  // full chunk
+            if (pl_k != pf.k) {
+              pl = prefetch_lanes(it.tb, it.slot0, it.hk, it.h, Hk, Hv, tile, tile * r + it.h - it.hk * r,
+                                  kDvTiles * r, l, q, k, v, rec);
+              pl_k = pf.k;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              if (pl.ptr[j]) touch(pl.ptr[j] + (size_t)pf.c * pl.adv[j], sink);
+          }
+          next_step(pf, gr, cu);
+        }
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        next_step(cur, gr, cu);
+      }
+    }
+    wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
+    return;
+  }
+
+  if (w >= kOutputWave0) {
+    // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  Q H
+    // is taken before b1 (H is rewritten in phase 3), P U~ after b2 (U~ is complete); the rows are
+    // staged and stored at the start of the next step.
+    const int ow = w - kOutputWave0;
+    Walker cur = first_step(gr, cu);
+    if (cur.valid) {
+      unsigned char *oslot = ostage + ow * kOBytes;
+      const uint32_t ooff = (uint32_t)(16 * ow + 4 * (l >> 4) + (l & 3)) * (uint32_t)(Hv * kDim * 2) +
+                            8 * ((l & 15) >> 2);
+      PFrags pf;
+      load_p(pf, rec_at(rec, cur.it.slot0, cur.it.h, Hv), ow, l);
+      Walker prev = cur;
+      __syncthreads();
+      for (int s = 0; cur.valid; ++s) {
+        if (s > 0)
+          store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
+                        reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
+        const f32x4 O = out_qh(tiles + (s % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
+        __syncthreads();  // b1
+        __syncthreads();  // b2
+        out_stage(O, pf, decs + (s % kDecStages) * kDecBytes, Uo, ow, l, oslot);
+        Walker nx = cur;
+        next_step_clamped(nx, gr, cu);
+        load_p(pf, rec_at(rec, nx.it.slot0 + nx.c, nx.it.h, Hv), ow, l);
+        __syncthreads();  // b3
+        prev = cur;
+        next_step(cur, gr, cu);
+      }
+      store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
+                    reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
+    }
+    return;
+  }
+
+  if (w >= kComputeWaves) {
+    // Producer waves.  Barriers: one before the loop, three per step, as the compute waves.
+    const int pw = w - kComputeWaves;
+    Walker cur = first_step(gr, cu);
+    if (cur.valid) {
+      const unsigned tiles_lds = (unsigned)(uintptr_t)tiles;
+      const unsigned decs_lds = (unsigned)(uintptr_t)decs;
+      ProducerLanes pl;
+      pl.row0 = 4 * pw + (l >> 4);
+      pl.lc = (l & 15) ^ (pl.row0 & 15);
+      pl.tile = (uint32_t)pl.row0 * (uint32_t)(Hk * kDim * 2) + 16 * pl.lc;
+      pl.v = (uint32_t)(l >> 1) * (uint32_t)(Hv * kDim * 2) + 2 * (d0 + 8 * (l & 1));
+      // K, Q and V bases (bytes, row 0) of a step's head
+#define GDN_BASES(W)                                                                              \
+  reinterpret_cast<const unsigned char *>(k + (size_t)(W).it.hk * kDim),                          \
+      reinterpret_cast<const unsigned char *>(q + (size_t)(W).it.hk * kDim),                      \
+      reinterpret_cast<const unsigned char *>(v + (size_t)(W).it.h * kDim)
+      Walker ld = cur;  // step 0, then 1
+      dma_tiles_all(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld),
+                    rec_at(rec, ld.it.slot0 + ld.c, ld.it.h, Hv), pl, tiles_lds);
+      if (pw == kDecWave) dma_dec(ld.it.slot0 + ld.c, ld.it.h, Hv, l, rec, decs_lds);
+      next_step_clamped(ld, gr, cu);
+      dma_tiles_all(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld),
+                    rec_at(rec, ld.it.slot0 + ld.c, ld.it.h, Hv), pl, tiles_lds + kTileBytes);
+      if (pw == kDecWave) dma_dec(ld.it.slot0 + ld.c, ld.it.h, Hv, l, rec, decs_lds + kDecBytes);
+      // step 0 has landed: only step 1's loads may still be in flight
+      if (pw == 3) wait_vmcnt<kChunkCount(3)>();
+      else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
+      else wait_vmcnt<kChunkCount(0)>();
+      __syncthreads();
+      for (int s = 0; cur.valid; ++s) {
+        // Step s + 2 is loaded during step s, spread over its three phases, into tile and decay
+        // slots (s + 2) % 3, which held step s - 1 (clamped reloads of the last step only go to
+        // slots that are no longer read): K before b1, Q before b2, V and the decays before b3.
+        next_step_clamped(ld, gr, cu);
+        const unsigned tslot = tiles_lds + ((s + 2) % kTileStages) * kTileBytes;
+        const uint8_t *tp = rec_at(rec, ld.it.slot0 + ld.c, ld.it.h, Hv);
+        dma_tiles<0>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
+        __syncthreads();  // b1
+        dma_tiles<1>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
+        __syncthreads();  // b2
+        dma_tiles<2>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
+        if (pw == kDecWave)
+          dma_dec(ld.it.slot0 + ld.c, ld.it.h, Hv, l, rec, decs_lds + ((s + 2) % kDecStages) * kDecBytes);
+        // Step s + 1 (loaded during step s - 1) must have landed before b3: loads complete in
+        // issue order, so it is enough that at most this iteration's loads are in flight.
+        if (pw == 3) wait_vmcnt<kChunkCount(3)>();
+        else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
+        else wait_vmcnt<kChunkCount(0)>();
+        __syncthreads();  // b3
+        next_step(cur, gr, cu);
+      }
+#undef GDN_BASES
+    }
+    wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
+    return;
+  }
+
+  // Compute waves.  State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].
+  // At the last chunk of an item the final state is stored and the next item's initial state,
+  // loaded during that chunk, takes its place before bf16 H goes to LDS.
+  Walker cur;
+  cur.k = -1;
+  next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
+  if (!cur.valid) return;
+  f32x4 H[2], Hn[2];
+  load_h0(H, cur.it, h0, h0_index, num_h0, Hv, d0, w, l);
+  write_ht(Ht, H, w, l);
+  __syncthreads();
+  for (int s = 0; cur.valid; ++s) {
+    const bool last = cur.c == cur.it.nc - 1;
+    Walker nx = cur;
+    if (last) {
+      next_item(nx, gr, cu);  // the next item's initial state (copies of empty items come later)
+      if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
+    }
+    chunk_step<false>(tiles + (s % kTileStages) * kTileBytes, decs + (s % kDecStages) * kDecBytes, w,
+                      l, H, Ht, Rh, Rl, Uh, Ul, Uo);
+    if (last) {
+      store_ht(H, cur.it, hT, Hv, d0, w, l);
+      next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
+      if (cur.valid) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) H[a] = Hn[a];
+      }
+    } else {
+      ++cur.c;
+    }
+    write_ht(Ht, H, w, l);
+    __syncthreads();  // b3
+  }
+}
+
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
-                       const void *rec, int64_t T, int N, int Hk, int Hv, hipStream_t stream) {
-  const unsigned nblocks = (unsigned)N * (unsigned)Hv * kDvTiles;
+                       const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
+                       hipStream_t stream) {
+  // Items: N Hv 8 (a multiple of 8).  One round when they fit on the device at one workgroup per
+  // CU (max_groups, a multiple of 8), else max_groups persistent workgroups.
+  const int total = N * Hv * kDvTiles;
+  const int G = total <= max_groups ? total : max_groups;
   const bool o_nt = (uint64_t)T * (uint64_t)Hv * kDim * 2 <= kOStreamBytes;
-  hipLaunchKernelGGL(o_nt ? state_pass_kernel<true> : state_pass_kernel<false>, dim3(nblocks),
-                     dim3(kThreads), 0, stream,
-                     static_cast<const unsigned short *>(q), static_cast<const unsigned short *>(k),
-                     static_cast<const unsigned short *>(v), cu, h0, h0_index, num_h0,
-                     static_cast<unsigned short *>(o), hT, static_cast<const uint8_t *>(rec), Hk, Hv);
+  const unsigned short *q16 = static_cast<const unsigned short *>(q);
+  const unsigned short *k16 = static_cast<const unsigned short *>(k);
+  const unsigned short *v16 = static_cast<const unsigned short *>(v);
+  unsigned short *o16 = static_cast<unsigned short *>(o);
+  const uint8_t *r8 = static_cast<const uint8_t *>(rec);
+  if (G == total)
+    hipLaunchKernelGGL(o_nt ? state_pass_kernel<true> : state_pass_kernel<false>, dim3(G),
+                       dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0, o16, hT,
+                       r8, Hk, Hv);
+  else
+    hipLaunchKernelGGL(o_nt ? state_pass_multi_kernel<true> : state_pass_multi_kernel<false>,
+                       dim3(G), dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0,
+                       o16, hT, r8, Hk, Hv, total);
 }
 
 }  // namespace gdn

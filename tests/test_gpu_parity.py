@@ -159,3 +159,39 @@ def test_empty_batch_keeps_state():
     x.h0 = None
     o, hT = run_gpu(x)
     assert np.all(hT == 0)
+
+
+def test_many_sequences_persistent_pass():
+    # 40 sequences x 4 v-heads x 8 column tiles = 1280 work items, more than one round of
+    # workgroups on the device: each workgroup walks several items (empty ones included) as one
+    # stream of chunks.  Parity against the oracle, and bitwise equality with separate calls of
+    # one sequence each (one item per workgroup).
+    rng = np.random.default_rng(90)
+    lengths = [int(x) for x in rng.choice([0, 1, 37, 64, 65, 130, 200], size=40)]
+    lengths[3] = 0
+    lengths[4] = 0
+    say(f"[persistent] 40 sequences, lengths {lengths}")
+    x = gi.make_gdn_inputs(2, 4, lengths, seed=91, with_h0=True)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), "40 sequences")
+    cu = x.cu
+    for n in (0, 3, 7, 21, 39):
+        L = lengths[n]
+        sl = slice(cu[n], cu[n + 1])
+        xs = gi.GdnInputs(x.q[sl], x.k[sl], x.v[sl], x.beta[sl], x.g[sl], np.array([0, L], np.int32),
+                          x.h0[n:n + 1])
+        o1, h1 = run_gpu(xs)
+        assert np.array_equal(o[sl], o1), f"sequence {n}: output differs"
+        assert np.array_equal(hT[n], h1[0]), f"sequence {n}: state differs"
+    # the same batch with the initial states drawn from a pool by index (two rows, and zeros)
+    index = np.array([i % 3 - 1 for i in range(40)], dtype=np.int32)  # -1, 0, 1, -1, ...
+    pool = x.h0[:2]
+    d = dev_inputs(x)
+    oi, hi = gdn.gdn_chunk_fwd_indexed(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"],
+                                       torch.from_numpy(pool).cuda(), torch.from_numpy(index).cuda(),
+                                       cu_seqlens_host=torch.from_numpy(cu.astype(np.int64)))
+    torch.cuda.synchronize()
+    gathered = np.stack([pool[i] if i >= 0 else np.zeros_like(pool[0]) for i in index])
+    xg = gi.GdnInputs(x.q, x.k, x.v, x.beta, x.g, x.cu, gathered)
+    og, hg = run_gpu(xg)
+    assert np.array_equal(oi.float().cpu().numpy(), og) and np.array_equal(hi.cpu().numpy(), hg)
