@@ -15,6 +15,9 @@
 //   3. From the accumulators, per v-head:
 //        A_ij = beta_i e^{G_i - G_j} (k_i . k_j)  for i > j      (fp32, LDS)
 //        P_ij = e^{G_i - G_j} (q_i . k_j)         for i >= j     (bf16, straight to the record)
+//      Off the diagonal blocks the decay is a product of two tabulated factors,
+//      e^{G_i - G_r} e^{G_r - G_j} with r the first token of i's 16-row block (j < r <= i, so both
+//      exponents are <= 0); only the diagonal blocks take one exponential per entry.
 //   4. T = (I + A)^-1: each 16x16 diagonal block by right-looking substitution (four lanes per
 //      column), then block column j by T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA, with
 //      the column's blocks kept in registers, one wave per block column (no barrier in between).
@@ -42,7 +45,11 @@ constexpr int kOffA = 0;                                   // + x * kMatBytes
 constexpr int kOffT = kMaxHeads * kMatBytes;               // 34816 + x * kMatBytes
 constexpr int kOffG = 2 * kMaxHeads * kMatBytes;           // 69632: G[x][64]
 constexpr int kOffB = kOffG + kMaxHeads * kChunk * 4;      // beta[x][64]
-constexpr int kLdsBytes = kOffB + kMaxHeads * kChunk * 4;  // 70656: two workgroups per CU
+// Decay factors: Er[x][i] = e^{G_i - G_{16 (i / 16)}}; Fc[x][rb - 1][j] = e^{G_{16 rb} - G_j} for
+// j < 16 rb, rb = 1..3.
+constexpr int kOffEr = kOffB + kMaxHeads * kChunk * 4;
+constexpr int kOffFc = kOffEr + kMaxHeads * kChunk * 4;
+constexpr int kLdsBytes = kOffFc + kMaxHeads * 3 * kChunk * 4;  // 72704: two workgroups per CU
 static_assert(kMaxHeads * kMatBytes >= 2 * kChunk * kDim * 2, "the A matrices cover Ks and Qs");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -113,6 +120,8 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   unsigned char *Qs = smem + kOffQs;
   float *Gall = reinterpret_cast<float *>(smem + kOffG);
   float *Ball = reinterpret_cast<float *>(smem + kOffB);
+  float *Erall = reinterpret_cast<float *>(smem + kOffEr);
+  float *Fcall = reinterpret_cast<float *>(smem + kOffFc);
 
   // Workgroup b runs on XCD b % 8.  For one sequence the state pass keeps v-heads
   // [x Hv / 8, (x + 1) Hv / 8) on XCD x; dealing the (slot, head group) units out the same way puts
@@ -166,12 +175,16 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   const float bv = l < L ? b_raw : 0.f;
   const float G = wave_inclusive_scan(gv);
   const float Glast = __shfl(G, 63, 64);
+  const float Gref = __shfl(G, wl == 0 ? (l & ~15) : 16 * wl, 64);
   if (wl == 0) {
     Gall[kChunk * hh + l] = G;
     Ball[kChunk * hh + l] = bv;
+    Erall[kChunk * hh + l] = exp_neg(G - Gref);
     uint8_t *R = rec_slot + (size_t)h * kRecBytes;
     __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
     __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
+  } else {
+    Fcall[kChunk * (3 * hh + wl - 1) + l] = l < 16 * wl ? exp_neg(Gref - G) : 0.f;
   }
   __syncthreads();
 
@@ -218,12 +231,25 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
 #pragma unroll
       for (int x = 0; x < HP; ++x) {
         const float *Gx = Gall + kChunk * x;
-        const float Gi = Gx[i];
-        const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gx + j0);
+        // Decays e^{G_i - G_j}, j = j0 .. j0 + 3: tabulated factors off the diagonal blocks.
+        f32x4 e;
+        if (rb != cb) {
+          const float ei = Erall[kChunk * x + i];
+          const f32x4 fj = *reinterpret_cast<const f32x4 *>(Fcall + kChunk * (3 * x + rb - 1) + j0);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) e[rr] = ei * fj[rr];
+        }
         if (which) {
           float d[4];
+          if (rb != cb) {
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) d[rr] = j0 + rr <= i ? exp_neg(Gi - Gj[rr]) * acc[it][rr] : 0.f;
+            for (int rr = 0; rr < 4; ++rr) d[rr] = e[rr] * acc[it][rr];
+          } else {
+            const float Gi = Gx[i];
+            const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gx + j0);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) d[rr] = j0 + rr <= i ? exp_neg(Gi - Gj[rr]) * acc[it][rr] : 0.f;
+          }
           const u32x2 val = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
           uint8_t *dst = rec_slot + (size_t)(h_first + x) * kRecBytes + kRecP +
                          frag_index(rb, cb >> 1) * kFragBytes + l * 16 + 8 * (cb & 1);
@@ -239,8 +265,10 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
           if (rb != cb) {
             const float bi = Ball[kChunk * x + i];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) av[rr] = bi * exp_neg(Gi - Gj[rr]) * acc[it][rr];
+            for (int rr = 0; rr < 4; ++rr) av[rr] = bi * e[rr] * acc[it][rr];
           } else {
+            const float Gi = Gx[i];
+            const f32x4 Gj = *reinterpret_cast<const f32x4 *>(Gx + j0);
             const f32x4 bj = *reinterpret_cast<const f32x4 *>(Ball + kChunk * x + j0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
@@ -288,8 +316,10 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   // registers (C layout: lane (col lj, rows 4 lg + rr)); in every product the k-slot (step s,
   // lane group lg) stands for row 4 lg + s of the B operand, so an accumulator is fed back as B
   // without moving data between lanes.
+  // Wave w runs on SIMD w % 4; the second v-head takes the block columns in reverse order, so the
+  // long chain of column 0 never shares a SIMD's matrix unit with the other head's.
   {
-    const int j = wl;
+    const int j = hh ? 3 - wl : wl;
     // A operands (row lj, cols 4 lg + s): Aj[i] = A_ij, Am[i][m] = A_im (j < m < i), Tii[i] = T_ii;
     // every register array index is a compile-time constant (j is not).
     f32x4 Aj[4], Am[4][4], Tii[4], Tjj;
@@ -340,15 +370,18 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   __syncthreads();
 
   // ---- 5. T' = T diag(beta) as bf16 hi/lo fragments -------------------------------------------
-  // Fragment f, lane ll: row i = 16 rb(f) + ll % 16, columns 32 ks(f) + 8 (ll / 16) .. + 7.
-  uint8_t *R = rec_slot + (size_t)h * kRecBytes;
-  const float *Bh = Ball + kChunk * hh;
-  for (int task = 64 * wl + l; task < kFrags * 64; task += 256) {
+  // Fragment f, lane ll: row i = 16 rb(f) + ll % 16, columns 32 ks(f) + 8 (ll / 16) .. + 7.  The
+  // (v-head, fragment) tasks of the group are dealt over all its waves.
+  for (int u = tid; u < HP * kFrags * 64; u += kThreads) {
+    const int x = u / (kFrags * 64), task = u - x * (kFrags * 64);
     const int f = task >> 6, ll = task & 63;
+    uint8_t *R = rec_slot + (size_t)(h_first + x) * kRecBytes;
+    const float *Bh = Ball + kChunk * x;
+    const float *Tx = reinterpret_cast<const float *>(smem + kOffT + x * kMatBytes);
     const int i = 16 * frag_row_block(f) + (ll & 15);
     const int c0 = 32 * frag_k_step(f) + 8 * (ll >> 4);
-    const f32x4 m0 = *reinterpret_cast<const f32x4 *>(Ts + i * kPitchF + c0);
-    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(Ts + i * kPitchF + c0 + 4);
+    const f32x4 m0 = *reinterpret_cast<const f32x4 *>(Tx + i * kPitchF + c0);
+    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(Tx + i * kPitchF + c0 + 4);
     const f32x4 b0 = *reinterpret_cast<const f32x4 *>(Bh + c0);
     const f32x4 b1 = *reinterpret_cast<const f32x4 *>(Bh + c0 + 4);
     float t[8];
