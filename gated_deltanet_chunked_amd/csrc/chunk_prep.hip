@@ -109,12 +109,15 @@ __device__ __forceinline__ int block_row(int b) { return b < 1 ? 0 : (b < 3 ? 1 
 
 }  // namespace
 
-template <int HP>
-__global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
+// HP v-heads per workgroup, WPH waves per v-head (4, or 8 when all workgroups fit on the device at
+// once: the products, A/P and T' phases spread over twice the waves; the diagonal solve and the
+// column chains stay on the first 4 waves of each head).
+template <int HP, int WPH>
+__global__ __launch_bounds__(64 * WPH * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec) {
-  constexpr int kThreads = 256 * HP, kWaves = 4 * HP;
+  constexpr int kThreads = 64 * WPH * HP, kWaves = WPH * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   unsigned char *Ks = smem + kOffKs;
   unsigned char *Qs = smem + kOffQs;
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   const int h_first = grp * HP, hk = h_first / (Hv / Hk);
   const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = w >> 2, wl = w & 3;  // this wave's v-head within the group, wave within the head
+  const int hh = w / WPH, wl = w % WPH;  // this wave's v-head within the group, wave within the head
   const int h = h_first + hh;
 
   int tb = 0, te = T, n = 0;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   const float bv = l < L ? b_raw : 0.f;
   const float G = wave_inclusive_scan(gv);
   const float Glast = __shfl(G, 63, 64);
-  const float Gref = __shfl(G, wl == 0 ? (l & ~15) : 16 * wl, 64);
+  const float Gref = __shfl(G, wl == 0 ? (l & ~15) : 16 * (wl & 3), 64);
   if (wl == 0) {
     Gall[kChunk * hh + l] = G;
     Ball[kChunk * hh + l] = bv;
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
     uint8_t *R = rec_slot + (size_t)h * kRecBytes;
     __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
     __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
-  } else {
+  } else if (wl < 4) {
     Fcall[kChunk * (3 * hh + wl - 1) + l] = l < 16 * wl ? exp_neg(Gref - G) : 0.f;
   }
   __syncthreads();
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   // lane 4 cj + m / 4) across the lane quad and subtracts A[i][m] x_m from every row i; A[i][m]
   // is 0 for i <= m (A is strictly lower), so no row needs masking.  The 15 columns of A that the
   // steps use sit contiguously in the transposed diagonal-block storage and are read up front.
-  {
+  if (wl < 4) {
     const int o = 16 * wl, cj = l >> 2, r = l & 3;
     f32x4 ac[15];  // ac[m][e] = A[o + 4 r + e][o + m]
 #pragma unroll
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
   // without moving data between lanes.
   // Wave w runs on SIMD w % 4; the second v-head takes the block columns in reverse order, so the
   // long chain of column 0 never shares a SIMD's matrix unit with the other head's.
-  {
+  if (wl < 4) {
     const int j = hh ? 3 - wl : wl;
     // A operands (row lj, cols 4 lg + s): Aj[i] = A_ij, Am[i][m] = A_im (j < m < i), Tii[i] = T_ii;
     // every register array index is a compile-time constant (j is not).
@@ -403,16 +406,18 @@ __global__ __launch_bounds__(256 * HP) void chunk_prep_kernel(
 
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, hipStream_t stream) {
+                       void *rec, int max_groups, hipStream_t stream) {
   const unsigned short *qp = static_cast<const unsigned short *>(q);
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
-  if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
-    hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)nslots, (unsigned)(Hv / 2)), dim3(512), 0,
-                       stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
-  else
-    hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)nslots, (unsigned)Hv), dim3(256), 0,
-                       stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
+  const int hp = (Hv / Hk) % 2 == 0 ? 2 : 1;  // pairs of v-heads of one k-head per workgroup
+  const dim3 grid((unsigned)nslots, (unsigned)(Hv / hp));
+  // 8 waves per v-head when every workgroup has a CU of its own (one at a time fits by registers)
+  const bool wide = (int64_t)nslots * (Hv / hp) <= max_groups;
+  auto kern = hp == 2 ? (wide ? chunk_prep_kernel<2, 8> : chunk_prep_kernel<2, 4>)
+                      : (wide ? chunk_prep_kernel<1, 8> : chunk_prep_kernel<1, 4>);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * hp * (wide ? 8 : 4)), 0, stream, qp, kp, g, beta, cu, (int)T, N,
+                     Hk, Hv, rp);
 }
 
 }  // namespace gdn
