@@ -6,7 +6,7 @@
 // side while only the state is passed in sequence.  This kernel does all of that state-independent
 // work for every (chunk, v-head) at once; the sequential part lives in state_pass.hip.
 //
-// One workgroup per (chunk slot, HP = 1 or 2 v-heads of one k-head), 4 waves per v-head.  Every
+// One workgroup per (chunk slot, HP = 1 or 2 v-heads of one k-head), 8 waves per v-head.  Every
 // v-head of a k-head shares K K^T and Q K^T (only the decays and beta tell them apart), so a pair
 // of them shares the products and the q/k loads:
 //   1. G = inclusive cumsum of g over the chunk per v-head (a wave64 scan: 64 tokens = 64 lanes).
@@ -109,15 +109,16 @@ __device__ __forceinline__ int block_row(int b) { return b < 1 ? 0 : (b < 3 ? 1 
 
 }  // namespace
 
-// HP v-heads per workgroup, WPH waves per v-head (4, or 8 when all workgroups fit on the device at
-// once: the products, A/P and T' phases spread over twice the waves; the diagonal solve and the
-// column chains stay on the first 4 waves of each head).
-template <int HP, int WPH>
-__global__ __launch_bounds__(64 * WPH * HP) void chunk_prep_kernel(
+// HP v-heads per workgroup, kWavesPerHead waves per v-head: the products, the A/P scaling and the
+// T' fragments spread over all of them; the diagonal solve and the column chains run on the first
+// 4 waves of each head.
+constexpr int kWavesPerHead = 8;
+template <int HP>
+__global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec) {
-  constexpr int kThreads = 64 * WPH * HP, kWaves = WPH * HP;
+  constexpr int kThreads = 64 * kWavesPerHead * HP, kWaves = kWavesPerHead * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   unsigned char *Ks = smem + kOffKs;
   unsigned char *Qs = smem + kOffQs;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(64 * WPH * HP) void chunk_prep_kernel(
   const int h_first = grp * HP, hk = h_first / (Hv / Hk);
   const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = w / WPH, wl = w % WPH;  // this wave's v-head within the group, wave within the head
+  const int hh = w / kWavesPerHead, wl = w % kWavesPerHead;  // v-head within the group, wave within it
   const int h = h_first + hh;
 
   int tb = 0, te = T, n = 0;
@@ -406,18 +407,16 @@ __global__ __launch_bounds__(64 * WPH * HP) void chunk_prep_kernel(
 
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, int max_groups, hipStream_t stream) {
+                       void *rec, hipStream_t stream) {
   const unsigned short *qp = static_cast<const unsigned short *>(q);
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
-  const int hp = (Hv / Hk) % 2 == 0 ? 2 : 1;  // pairs of v-heads of one k-head per workgroup
-  const dim3 grid((unsigned)nslots, (unsigned)(Hv / hp));
-  // 8 waves per v-head when every workgroup has a CU of its own (one at a time fits by registers)
-  const bool wide = (int64_t)nslots * (Hv / hp) <= max_groups;
-  auto kern = hp == 2 ? (wide ? chunk_prep_kernel<2, 8> : chunk_prep_kernel<2, 4>)
-                      : (wide ? chunk_prep_kernel<1, 8> : chunk_prep_kernel<1, 4>);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * hp * (wide ? 8 : 4)), 0, stream, qp, kp, g, beta, cu, (int)T, N,
-                     Hk, Hv, rp);
+  if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
+    hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)nslots, (unsigned)(Hv / 2)),
+                       dim3(128 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
+  else
+    hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)nslots, (unsigned)Hv),
+                       dim3(64 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
 }
 
 }  // namespace gdn

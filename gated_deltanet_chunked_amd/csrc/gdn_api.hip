@@ -12,7 +12,7 @@
 namespace gdn {
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, int max_groups, hipStream_t stream);
+                       void *rec, hipStream_t stream);
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                        const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
@@ -175,8 +175,7 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
   unsigned char *rec = static_cast<unsigned char *>(ws);
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   if ((stage & kPrep) && s.T > 0) {
-    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec,
-                           device_max_groups(), stream);
+    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
   }
