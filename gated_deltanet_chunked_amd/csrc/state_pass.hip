@@ -605,7 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Uh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ul[kXBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Uo[2 * kXBytes];  // chunk c in Uo[c % 2]
   __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
   __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
 
@@ -658,8 +658,10 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
 
   if (w >= kOutputWave0) {
     // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  Q H
-    // is taken before b1 (the Q tile's slot is refilled after b1, H is rewritten in phase 3), P U~
-    // after b2 (U~ is complete); the rows are staged and stored at the start of the next chunk.
+    // of chunk c is taken between b1 and b2 (H(c) is rewritten in phase 3; the Q tile's slot is
+    // refilled during chunk c + 1), P U~ of chunk c before b1 of chunk c + 1 (U~ alternates between
+    // two buffers), so that nothing of the output path holds b3; the rows are stored between b1 and
+    // b2 of chunk c + 1.
     const int ow = w - kOutputWave0;
     if (nc > 0) {
       unsigned char *ob = reinterpret_cast<unsigned char *>(o + (size_t)h * kDim + d0);
@@ -668,16 +670,22 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
                             8 * ((l & 15) >> 2);
       PFrags pf;
       load_p(pf, rec_at(rec, slot0, h, Hv), ow, l);
+      f32x4 O = zero4();
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
-        if (c > 0) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
-        const f32x4 O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
+        if (c > 0) {
+          out_stage(O, pf, decs + ((c - 1) % kDecStages) * kDecBytes, Uo + ((c - 1) & 1) * kXBytes, ow, l,
+                    oslot);
+          load_p(pf, rec_at(rec, slot0 + c, h, Hv), ow, l);
+        }
         __syncthreads();  // b1
+        if (c > 0) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+        O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
-        out_stage(O, pf, decs + (c % kDecStages) * kDecBytes, Uo, ow, l, oslot);
-        load_p(pf, rec_at(rec, slot0 + min(c + 1, nc - 1), h, Hv), ow, l);
         __syncthreads();  // b3
       }
+      out_stage(O, pf, decs + ((nc - 1) % kDecStages) * kDecBytes, Uo + ((nc - 1) & 1) * kXBytes, ow, l,
+                oslot);
       store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
     }
     return;
@@ -757,7 +765,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     __syncthreads();
     for (int c = 0; c < nc; ++c)
       chunk_step<true>(tiles + (c % kTileStages) * kTileBytes, decs + (c % kDecStages) * kDecBytes, w,
-                       l, H, Ht, Rh, Rl, Uh, Ul, Uo);
+                       l, H, Ht, Rh, Rl, Uh, Ul, Uo + (c & 1) * kXBytes);
   }
 
   if (hT) {
@@ -786,7 +794,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Uh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ul[kXBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Uo[2 * kXBytes];  // chunk c in Uo[c % 2]
   __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
   __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
 
@@ -836,9 +844,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   }
 
   if (w >= kOutputWave0) {
-    // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  Q H
-    // is taken before b1 (H is rewritten in phase 3), P U~ after b2 (U~ is complete); the rows are
-    // staged and stored at the start of the next step.
+    // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  As in
+    // the single-round kernel: Q H of step s between b1 and b2, P U~ of step s before b1 of step
+    // s + 1, the rows stored between b1 and b2 of step s + 1.
     const int ow = w - kOutputWave0;
     Walker cur = first_step(gr, cu);
     if (cur.valid) {
@@ -848,22 +856,27 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       PFrags pf;
       load_p(pf, rec_at(rec, cur.it.slot0, cur.it.h, Hv), ow, l);
       Walker prev = cur;
+      f32x4 O = zero4();
+      int s = 0;
       __syncthreads();
-      for (int s = 0; cur.valid; ++s) {
+      for (; cur.valid; ++s) {
+        if (s > 0) {
+          out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo + ((s - 1) & 1) * kXBytes, ow, l,
+                    oslot);
+          load_p(pf, rec_at(rec, cur.it.slot0 + cur.c, cur.it.h, Hv), ow, l);
+        }
+        __syncthreads();  // b1
         if (s > 0)
           store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
                         reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
-        const f32x4 O = out_qh(tiles + (s % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
-        __syncthreads();  // b1
+        O = out_qh(tiles + (s % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
-        out_stage(O, pf, decs + (s % kDecStages) * kDecBytes, Uo, ow, l, oslot);
-        Walker nx = cur;
-        next_step_clamped(nx, gr, cu);
-        load_p(pf, rec_at(rec, nx.it.slot0 + nx.c, nx.it.h, Hv), ow, l);
         __syncthreads();  // b3
         prev = cur;
         next_step(cur, gr, cu);
       }
+      out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo + ((s - 1) & 1) * kXBytes, ow, l,
+                oslot);
       store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
                     reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
     }
@@ -947,7 +960,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
     }
     chunk_step<false>(tiles + (s % kTileStages) * kTileBytes, decs + (s % kDecStages) * kDecBytes, w,
-                      l, H, Ht, Rh, Rl, Uh, Ul, Uo);
+                      l, H, Ht, Rh, Rl, Uh, Ul, Uo + (s & 1) * kXBytes);
     if (last) {
       store_ht(H, cur.it, hT, Hv, d0, w, l);
       next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
