@@ -129,7 +129,7 @@ def test_h0_sensitivity_slow_decay():
     check(o, hT, *run_oracle(x), "slow decay")
 
 
-@pytest.mark.parametrize("Hk,Hv", [(4, 4), (2, 4), (1, 4), (16, 32)])
+@pytest.mark.parametrize("Hk,Hv", [(4, 4), (2, 4), (1, 4), (16, 32), (2, 6), (1, 8)])
 def test_head_ratios(Hk, Hv):
     say(f"[gqa] Hk={Hk} Hv={Hv}")
     x = gi.make_gdn_inputs(Hk, Hv, [97, 160], seed=100 + Hk * 10 + Hv, with_h0=True)
