@@ -49,7 +49,10 @@ constexpr int kOffB = kOffG + kMaxHeads * kChunk * 4;      // beta[x][64]
 // j < 16 rb, rb = 1..3.
 constexpr int kOffEr = kOffB + kMaxHeads * kChunk * 4;
 constexpr int kOffFc = kOffEr + kMaxHeads * kChunk * 4;
-constexpr int kLdsBytes = kOffFc + kMaxHeads * 3 * kChunk * 4;  // 72704: two workgroups per CU
+// Conv weights of the four 128-channel blocks (q, k, v, v; 4 taps, bf16) when the kernel makes q,
+// k, v itself.
+constexpr int kOffW = kOffFc + kMaxHeads * 3 * kChunk * 4;
+constexpr int kLdsBytes = kOffW + 4 * kDim * 4 * 2;  // 76800: two workgroups per CU
 static_assert(kMaxHeads * kMatBytes >= 2 * kChunk * kDim * 2, "the A matrices cover Ks and Qs");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -109,15 +112,29 @@ __device__ __forceinline__ int block_row(int b) { return b < 1 ? 0 : (b < 3 ? 1 
 
 }  // namespace
 
+// The GDN mixer's input prep done by the prep kernel itself (kConv): q, k, v from the packed
+// q | k | v input by a causal depthwise conv (4 taps, the carried window before a sequence start)
+// and SiLU, q and k L2-normalized per head -- the arithmetic of mixer_prep_kernel, token by token.
+// The workgroup of (slot, v-heads 2 p, 2 p + 1) makes the chunk's q and k of their k-head and v of
+// both v-heads, writes them for the state pass and keeps q, k in LDS for its own products.
+struct ConvArgs {
+  const unsigned short *qkv, *conv_w, *conv_in;
+  const int32_t *state_index;
+  int num_states;
+  unsigned short *qo, *ko, *vo;
+};
+
 // HP v-heads per workgroup, kWavesPerHead waves per v-head: the products, the A/P scaling and the
 // T' fragments spread over all of them; the diagonal solve and the column chains run on the first
 // 4 waves of each head.
 constexpr int kWavesPerHead = 8;
-template <int HP>
+template <int HP, bool kConv>
 __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec) {
+    const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec,
+    ConvArgs ca) {
+  static_assert(!kConv || HP == 2, "the input prep runs on pairs of v-heads");
   constexpr int kThreads = 64 * kWavesPerHead * HP, kWaves = kWavesPerHead * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
   unsigned char *Ks = smem + kOffKs;
@@ -157,24 +174,113 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
 
   // ---- 1. global loads up front; gate cumsum per v-head --------------------------------------
   constexpr int kIt = 1024 / kThreads;  // 16-byte pieces of one 64 x 128 tile per thread
-  u32x4 kv[kIt], qv[kIt];
+  if constexpr (kConv) {
+    // Waves 4 b .. 4 b + 3 make block b of the four 128-channel blocks q, k (k-head hk), v (v-heads
+    // h_first, h_first + 1); thread (token group tg, 8-channel group cg) makes channels cg * 8 .. + 7
+    // of tokens t0 + 4 tg .. + 3 from the 7 input rows its taps slide over.  Lanes 16 m .. 16 m + 15
+    // share a token group, so the L2 norm is a 16-lane butterfly.  With more than two v-heads per
+    // k-head the k-head's first pair writes q and k.  All input rows are loaded before anything is
+    // stored (the stores could alias the input for all the compiler knows), and the blocks' conv
+    // weights go through LDS once.
+    constexpr int kTok = 4;
+    const int blk = w >> 2, tl = tid & 255, tg = tl >> 4, cg = tl & 15;
+    const int C = (2 * Hk + Hv) * kDim;
+    auto seg_of = [&](int b) { return b == 0 ? hk : (b == 1 ? Hk + hk : 2 * Hk + h_first + b - 2); };
+    unsigned short *Ws = reinterpret_cast<unsigned short *>(smem + kOffW);
+    if (tid < 4 * kDim) {  // 8 bytes per thread: the 4 taps of one channel
+      const int b = tid / kDim, ch = tid % kDim;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2 *>(Ws + (b * kDim + ch) * 4) =
+          *reinterpret_cast<const u32x2 *>(ca.conv_w + (size_t)(seg_of(b) * kDim + ch) * 4);
+    }
+    const int tfirst = t0 + kTok * tg;
+    const unsigned short *win =
+        tfirst - 3 < tb ? window_of(ca.conv_in, ca.state_index, ca.num_states, n, (size_t)3 * C) : nullptr;
+    const int ch0 = seg_of(blk) * kDim + cg * 8;
+    const int tend = t0 + L;  // rows at or past it serve no token of this chunk
+    u16x8 xr[kTok + 3];
+    bool hv[kTok + 3];
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
-    const size_t off = ((size_t)(t0 + min(row, L - 1)) * Hk + hk) * kDim + ch * 8;
-    kv[it] = *reinterpret_cast<const u32x4 *>(k + off);
-    qv[it] = *reinterpret_cast<const u32x4 *>(q + off);
+    for (int i = 0; i < kTok + 3; ++i) {
+      const int src = tfirst - 3 + i;
+      hv[i] = src < tend && (src >= tb || win);
+      const unsigned short *row = src >= tb ? ca.qkv + (size_t)src * C : win + (size_t)(src - tb + 3) * C;
+      if (hv[i]) xr[i] = *reinterpret_cast<const u16x8 *>(row + ch0);
+    }
+    __syncthreads();  // the conv weights are in LDS
+    float wt[8][4];
+    {
+      const u16x8 *wp = reinterpret_cast<const u16x8 *>(Ws + (blk * kDim + cg * 8) * 4);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const u16x8 wv = wp[e2];  // taps of channels 2 e2, 2 e2 + 1
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wt[2 * e2][j] = bits_to_float(wv[j]);
+          wt[2 * e2 + 1][j] = bits_to_float(wv[4 + j]);
+        }
+      }
+    }
+    const bool write_qk = (h_first / 2) % ((Hv / Hk) / 2) == 0;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      const int r = kTok * tg + u, t = t0 + r;
+      const bool valid = r < L;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (hv[u + j]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += wt[e][j] * bits_to_float(xr[u + j][e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = silu(acc[e]);
+      }
+      if (blk < 2) {
+        float ss2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss2 += acc[e] * acc[e];
+        ss2 = sum16(ss2);
+        const float rn = rsqrt_hw(ss2 + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= rn;
+      }
+      u16x8 out;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = bf16_bits(to_bf16(acc[e]));
+      if (valid && (blk >= 2 || write_qk)) {
+        unsigned short *dst = blk == 0   ? ca.qo + ((size_t)t * Hk + hk) * kDim
+                              : blk == 1 ? ca.ko + ((size_t)t * Hk + hk) * kDim
+                                         : ca.vo + ((size_t)t * Hv + h_first + blk - 2) * kDim;
+        *reinterpret_cast<u16x8 *>(dst + cg * 8) = out;
+      }
+      if (blk < 2)  // zeros past L
+        *reinterpret_cast<u16x8 *>((blk == 0 ? Qs : Ks) + r * (kDim * 2) + ((cg ^ (r & 15)) << 4)) = out;
+    }
+  } else {
+    u32x4 kv[kIt], qv[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
+      const size_t off = ((size_t)(t0 + min(row, L - 1)) * Hk + hk) * kDim + ch * 8;
+      kv[it] = *reinterpret_cast<const u32x4 *>(k + off);
+      qv[it] = *reinterpret_cast<const u32x4 *>(q + off);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const int so = row * (kDim * 2) + ((ch ^ (row & 15)) << 4);
+      *reinterpret_cast<u32x4 *>(Ks + so) = row < L ? kv[it] : zero;
+      *reinterpret_cast<u32x4 *>(Qs + so) = row < L ? qv[it] : zero;
+    }
   }
   const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
   const float g_raw = g[gi], b_raw = beta[gi];
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int so = row * (kDim * 2) + ((ch ^ (row & 15)) << 4);
-    *reinterpret_cast<u32x4 *>(Ks + so) = row < L ? kv[it] : zero;
-    *reinterpret_cast<u32x4 *>(Qs + so) = row < L ? qv[it] : zero;
-  }
   const float gv = l < L ? g_raw : 0.f;
   const float bv = l < L ? b_raw : 0.f;
   const float G = wave_inclusive_scan(gv);
@@ -412,11 +518,30 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
   if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
-    hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)nslots, (unsigned)(Hv / 2)),
-                       dim3(128 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
+    hipLaunchKernelGGL((chunk_prep_kernel<2, false>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
+                       dim3(128 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
+                       ConvArgs{});
   else
-    hipLaunchKernelGGL(chunk_prep_kernel<1>, dim3((unsigned)nslots, (unsigned)Hv),
-                       dim3(64 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp);
+    hipLaunchKernelGGL((chunk_prep_kernel<1, false>), dim3((unsigned)nslots, (unsigned)Hv),
+                       dim3(64 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
+                       ConvArgs{});
+}
+
+// The same with q, k, v made from the packed mixer input (Hv / Hk even): writes q, k, v (q/k
+// [T, Hk, 128], v [T, Hv, 128], bf16) as the mixer's input prep does, and the records.
+void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
+                            const int32_t *state_index, int num_states, const float *g,
+                            const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
+                            int64_t nslots, void *rec, void *qo, void *ko, void *vo,
+                            hipStream_t stream) {
+  const ConvArgs ca{static_cast<const unsigned short *>(qkv), static_cast<const unsigned short *>(conv_w),
+                    static_cast<const unsigned short *>(conv_in), state_index, num_states,
+                    static_cast<unsigned short *>(qo), static_cast<unsigned short *>(ko),
+                    static_cast<unsigned short *>(vo)};
+  hipLaunchKernelGGL((chunk_prep_kernel<2, true>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
+                     dim3(128 * kWavesPerHead), 0, stream, (const unsigned short *)nullptr,
+                     (const unsigned short *)nullptr, g, beta, cu, (int)T, N, Hk, Hv,
+                     static_cast<uint8_t *>(rec), ca);
 }
 
 }  // namespace gdn

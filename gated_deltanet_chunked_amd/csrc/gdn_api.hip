@@ -17,6 +17,11 @@ void launch_state_pass(const void *q, const void *k, const void *v, const int32_
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                        const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
                        hipStream_t stream);
+void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
+                            const int32_t *state_index, int num_states, const float *g,
+                            const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
+                            int64_t nslots, void *rec, void *qo, void *ko, void *vo,
+                            hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, const void *conv_in, const int32_t *state_index,
                        int num_states, void *q, void *k, void *v, hipStream_t stream);
@@ -264,7 +269,8 @@ int gdn_state_pass(const gdn_chunk_desc *d, const void *q, const void *k, const 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Mixer: K0 (conv + SiLU + split + q/k L2 norm) -> chunk path -> K4 (gated RMSNorm).
+// Mixer: K0 (conv + SiLU + split + q/k L2 norm) -> chunk path -> K4 (gated RMSNorm); with Hv / Hk
+// even, K0 is done inside the chunk prep kernel.
 // Workspace: [chunk path | q' | k' | v' | o] with the prepped q/k/v and o in bf16.
 // ---------------------------------------------------------------------------------------------
 namespace {
@@ -343,7 +349,15 @@ int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *con
   unsigned char *vp = kp + m.q_bytes;
   unsigned char *op = vp + m.v_bytes;
   (void)hipGetLastError();
-  if (tok) {
+  // With pairs of v-heads per k-head the chunk prep makes q, k, v from qkv itself (one kernel
+  // instead of the input prep, then the chunk prep); otherwise the input prep runs first.
+  const bool fused = tok && (s.Hv / s.Hk) % 2 == 0;
+  if (fused) {
+    gdn::launch_chunk_prep_conv(qkv, conv_w, conv_in, state_index, num_states, g, beta, cu_seqlens,
+                                s.T, s.N, s.Hk, s.Hv, s.nslots, base, qp, kp, vp, strm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip(e);
+  } else if (tok) {
     gdn::launch_mixer_prep(qkv, conv_w, cu_seqlens, s.T, s.N, s.Hk, s.Hv, conv_in, state_index,
                            num_states, qp, kp, vp, strm);
     hipError_t e = hipGetLastError();
@@ -357,7 +371,7 @@ int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *con
     if (e != hipSuccess) return record_hip(e);
   }
   const StatePool pool{h0, num_states, state_index};
-  st = run_chunk(s, kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm);
+  st = run_chunk(s, fused ? kPass : kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm);
   if (st != GDN_OK) return st;
   if (tok) {
     gdn::launch_gated_rmsnorm(op, z, norm_w, d->norm_eps, s.T, s.Hv, y, strm);

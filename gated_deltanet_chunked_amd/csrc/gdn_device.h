@@ -100,6 +100,35 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 
 // Workgroups are dealt to the 8 XCDs round-robin (hardware id b runs on XCD b % 8).  Renumber
 // so that consecutive logical ids share an XCD and therefore its L2.
+// ---- GDN mixer input prep (conv + SiLU + L2 norm): shared by mixer_prep_kernel and the prep
+// kernel that makes q, k, v from the packed input itself ----
+// x sigmoid(x) with the hardware exp2 and reciprocal (each about 1 ulp): the result is rounded
+// to bf16 (8 bits) right after, far above their error.  Saturates correctly: exp2 overflows to
+// inf for x << 0 (result -0), underflows to 0 for x >> 0 (result x).
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+// 1 / sqrt(x) for x > 0 with the hardware reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+
+__device__ __forceinline__ float sum16(float x) {
+  // butterfly over the 16 lanes that share l / 16
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Carried conv window of sequence n ([W, C] bf16, oldest row first), or null for zeros.
+__device__ __forceinline__ const unsigned short *window_of(const unsigned short *conv_in,
+                                                           const int32_t *state_index,
+                                                           int num_states, int n, size_t rows) {
+  if (!conv_in) return nullptr;
+  const int r = state_index ? state_index[n] : n;
+  return (r >= 0 && r < num_states) ? conv_in + (size_t)r * rows : nullptr;
+}
+
+
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
   if (nblocks % 8 != 0) return bid;
   return (bid % 8) * (nblocks / 8) + bid / 8;

@@ -10,36 +10,6 @@
 
 namespace gdn {
 
-namespace {
-
-// x sigmoid(x) with the hardware exp2 and reciprocal (each about 1 ulp): the result is rounded
-// to bf16 (8 bits) right after, far above their error.  Saturates correctly: exp2 overflows to
-// inf for x << 0 (result -0), underflows to 0 for x >> 0 (result x).
-__device__ __forceinline__ float silu(float x) {
-  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
-}
-
-// 1 / sqrt(x) for x > 0 with the hardware reciprocal square root (about 1 ulp).
-__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
-
-__device__ __forceinline__ float sum16(float x) {
-  // butterfly over the 16 lanes that share l / 16
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
-
-// Carried conv window of sequence n ([W, C] bf16, oldest row first), or null for zeros.
-__device__ __forceinline__ const unsigned short *window_of(const unsigned short *conv_in,
-                                                           const int32_t *state_index,
-                                                           int num_states, int n, size_t rows) {
-  if (!conv_in) return nullptr;
-  const int r = state_index ? state_index[n] : n;
-  return (r >= 0 && r < num_states) ? conv_in + (size_t)r * rows : nullptr;
-}
-
-}  // namespace
-
 // Grid: (ceil(T / (16 kPrepTokens)), 2 Hk + Hv).  Block y selects a 128-channel head segment of
 // the packed q | k | v channels; each thread owns 8 channels x kPrepTokens consecutive tokens.
 // Lanes 16m .. 16m+15 of a wave hold the 16 channel groups of the same tokens, so the per-token

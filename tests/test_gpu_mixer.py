@@ -87,3 +87,14 @@ def test_mixer_varlen_bitwise_equals_separate():
                             np.array([0, L], np.int32), m.h0[n:n + 1])
         y1, h1 = run_mixer_gpu(ms, 2, 4)
         assert np.array_equal(y[sl], y1) and np.array_equal(hT[n], h1[0])
+
+
+@pytest.mark.parametrize("Hk,Hv", [(4, 4), (1, 4), (2, 6)])
+def test_mixer_head_ratios(Hk, Hv):
+    # Hv / Hk odd: the input prep runs as its own kernel before the chunk prep; even: the chunk
+    # prep makes q, k, v itself (with 4 v-heads per k-head, two workgroups make the same q, k and
+    # the first of them writes it).
+    lengths = [70, 1, 130]
+    say(f"[mixer] head ratio Hk={Hk} Hv={Hv} lengths={lengths} with h0")
+    m = gi.make_mixer_inputs(300 + 10 * Hk + Hv, lengths=lengths, Hk=Hk, Hv=Hv, with_h0=True)
+    check_mixer(*run_mixer_gpu(m, Hk, Hv), *run_mixer_oracle(m, Hk, Hv), f"Hk={Hk} Hv={Hv}", m)
