@@ -52,7 +52,7 @@ constexpr int kOffFc = kOffEr + kMaxHeads * kChunk * 4;
 // Conv weights of the four 128-channel blocks (q, k, v, v; 4 taps, bf16) when the kernel makes q,
 // k, v itself.
 constexpr int kOffW = kOffFc + kMaxHeads * 3 * kChunk * 4;
-constexpr int kLdsBytes = kOffW + 4 * kDim * 4 * 2;  // 76800: two workgroups per CU
+constexpr int kLdsBytes = kOffW + 4 * kDim * 4 * 2;  // 76800 with the conv weights, 72704 without: two workgroups per CU
 static_assert(kMaxHeads * kMatBytes >= 2 * kChunk * kDim * 2, "the A matrices cover Ks and Qs");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     ConvArgs ca) {
   static_assert(!kConv || HP == 2, "the input prep runs on pairs of v-heads");
   constexpr int kThreads = 64 * kWavesPerHead * HP, kWaves = kWavesPerHead * HP;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kConv ? kLdsBytes : kOffW];
   unsigned char *Ks = smem + kOffKs;
   unsigned char *Qs = smem + kOffQs;
   float *Gall = reinterpret_cast<float *>(smem + kOffG);
