@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR --copy-mib M [--workload NAME]
+    python bench.py --summarize-mfma PMC_DIR
 
 
 A step is one gdn_chunk_fwd over one batch of synthetic inputs already resident in HBM (for the
@@ -15,7 +16,9 @@ The second form turns two rocprofv3 counter runs of the first form (one with --p
 one with --pmc WRITE_SIZE, both with --copy-mib M) into profiles/traffic_<kernel>_<workload>.json:
 the counters of the dominant kernel per dispatch, each scaled by what the same counter reads for a
 plain device copy of M MiB, and a hash of the kernel's sources.  A later bench run reports that
-traffic in roofline.traffic only while the hash still matches.
+traffic in roofline.traffic only while the hash still matches.  The third form prints the MFMA
+utilisation of the chunk kernels from a rocprofv3 run with --pmc SQ_VALU_MFMA_BUSY_CYCLES
+SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE.
 
 Workloads (seeded, synthetic; see gdn_inputs.py):
     t539_h16x32      single sequence, T=539, Hk=16, Hv=32, d=128  (default)
@@ -158,6 +161,42 @@ def summarize_traffic(fetch_dir, write_dir, copy_mib, workload):
             log(f"[bench] {kern}: {rec['traffic_bytes'] / 1e6:.2f} MB per launch -> {traffic_path(kern, workload)}")
 
 
+def summarize_counters(run_dir):
+    """MFMA utilisation of the two chunk kernels from a rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F32 and
+    GRBM_GUI_ACTIVE.  GRBM_GUI_ACTIVE comes summed over the 8 XCDs, so the busy fraction is
+    busy / (GRBM_GUI_ACTIVE / 8 * SIMDs); a MOPS count is 512 flops.  Printed as a markdown table."""
+    import csv
+    import glob
+    simds = 256 * 4
+    per = {}
+    dur = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                kern = next((k for k, sym in KERNEL_SYMBOLS.items() if sym in r["Kernel_Name"]), None)
+                if kern is None:
+                    continue
+                key = (kern, int(r["Dispatch_Id"]))
+                d = per.setdefault(key, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    print("| kernel | dispatches | MFMA busy (of all SIMD cycles) | bf16 MFMA TFLOP/s (of 2,516.6) "
+          "| fp32 MFMA TFLOP/s | MFMA flops per dispatch (bf16 / fp32) | µs per dispatch under counters |")
+    print("|---|---|---|---|---|---|---|")
+    for kern in KERNEL_SYMBOLS:
+        keys = [k for k in per if k[0] == kern]
+        if not keys:
+            continue
+        busy = statistics.median(per[k]["SQ_VALU_MFMA_BUSY_CYCLES"] / (per[k]["GRBM_GUI_ACTIVE"] / 8 * simds)
+                                 for k in keys)
+        bf = statistics.median(per[k]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for k in keys)
+        f32 = statistics.median(per[k]["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512 for k in keys)
+        t = statistics.median(dur[k] for k in keys)
+        print(f"| {kern} | {len(keys)} | {busy:.3f} | {bf / t / 1e12:.1f} ({bf / t / 1e12 / BF16_PEAK_TFLOPS:.3f}) "
+              f"| {f32 / t / 1e12:.2f} | {bf / 1e9:.2f} G / {f32 / 1e9:.3f} G | {t * 1e6:.1f} |")
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
     try:
@@ -182,7 +221,13 @@ def main():
                     help="also run a plain device copy of this size (counter calibration under rocprofv3)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_*.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="print the chunk kernels' MFMA utilisation from a rocprofv3 --pmc run and exit")
     args = ap.parse_args()
+
+    if args.summarize_mfma:
+        summarize_counters(args.summarize_mfma)
+        return
 
     if args.summarize_traffic:
         if args.copy_mib <= 0:
