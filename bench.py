@@ -236,7 +236,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "requested_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
