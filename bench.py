@@ -97,11 +97,17 @@ KERNEL_SYMBOLS = {"state_pass": "state_pass_kernel", "chunk_prep": "chunk_prep_k
 
 
 def kernel_sha(kernel):
+    """Hash of the kernel's sources with comments and blank runs removed, so that an edit of the
+    comments alone does not mark its counter summary as stale."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -316,11 +316,11 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
 // The output path o = e^G o (Q H) + P U~ for row block w of a chunk, on the output wave that
 // shares a SIMD with compute wave w.  It issues no global->LDS loads: a wave's LDS reads wait for
 // its own global->LDS loads still in flight, which would tie these reads to load latency.  out_qh
-// runs before b1: Q H needs the chunk's entry state, which the compute waves overwrite in phase 3
-// (b1 is the natural point; the Q tile's slot is not refilled before chunk c + 1).  out_stage runs
-// after b2, once U~
-// is in LDS: it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg ..
-// + 3 of column lj at byte 8 l); they are read back transposed and stored at the start of the
+// runs between b1 and b2: Q H needs the chunk's entry state, which the compute waves overwrite in
+// phase 3, and the Q tile's slot is not refilled before chunk c + 1.  out_stage runs once U~ is in
+// LDS, after the chunk's last barrier and before b1 of the next chunk (U~ alternates between two
+// buffers): it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg .. + 3
+// of column lj at byte 8 l); they are read back transposed and stored between b1 and b2 of the
 // next chunk (store_o).
 __device__ __forceinline__ f32x4 out_qh(const unsigned char *qt, const unsigned char *Ht, int w, int l) {
   const int lj = l & 15, lg = l >> 4;
