@@ -285,6 +285,7 @@ int mixer_layout(const gdn_mixer_desc *d, MixerLayout &m) {
   if (d->conv_taps != 4) return GDN_ERR_UNSUPPORTED;
   if (!(d->norm_eps > 0.f)) return GDN_ERR_UNSUPPORTED;
   if (2 * (int64_t)m.s.Hk + m.s.Hv > 65535) return GDN_ERR_SHAPE;  // head segments on grid y
+  if ((m.s.T * m.s.Hv + 15) / 16 > INT32_MAX) return GDN_ERR_SHAPE;  // gated RMSNorm grid x
   m.chunk_bytes = m.s.rec_bytes;
   m.q_bytes = round_up((size_t)m.s.T * m.s.Hk * gdn::kDim * 2);
   m.v_bytes = round_up((size_t)m.s.T * m.s.Hv * gdn::kDim * 2);

@@ -163,6 +163,10 @@ def test_mixer_validation():
     assert call(good(), cw=a["k"] + 4) == gdn.GDN_ERR_ALIGN
     assert call(good(), nw=a["h0"] + GB // 2 + 4) == gdn.GDN_ERR_ALIGN
     assert call(good(), y=a["v"]) == gdn.GDN_ERR_ALIAS          # y over z
+    # T * Hv rows of the gated RMSNorm beyond one grid of 16-row blocks
+    big = gdn.MixerDesc(gdn.ChunkDesc(2 ** 31 - 256, 1, 1, 32, 128, 128, a["ws"], ws), 4, 1e-6)
+    assert gdn.gdn_mixer_fwd_workspace_size(2 ** 31 - 256, 1, 1, 32) == 0
+    assert call(big) == gdn.GDN_ERR_SHAPE
 
 
 def _call_indexed(num_h0=3, idx=None, **over):
