@@ -143,10 +143,22 @@ def _check_cu(cu_seqlens, T, cu_host):
     return host.numel() - 1
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The stream to enqueue on: the given one, else the current stream of the tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _workspace(workspace, need, device):
+    """A caller's workspace (uint8, contiguous, on the device, at least `need` bytes), or a new one."""
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    return workspace
 
 
 def _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace, cu_seqlens_host):
@@ -170,8 +182,7 @@ def _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace, cu_seq
     need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
     if need == 0:
         raise GdnError(GDN_ERR_SHAPE, "gdn_chunk_fwd_workspace_size")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     return T, N, Hk, Hv, o, hT, _desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel())
 
 
@@ -187,7 +198,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, wan
     if h0 is not None:
         _check(h0, "h0", torch.float32, (N, Hv, D, D), q.device)
     rc = lib().gdn_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                             _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
+                             _ptr(h0), _ptr(o), _ptr(hT), _stream(stream, q.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd")
     return o, hT
@@ -207,7 +218,7 @@ def gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, *, o=None,
     _check(h0_index, "h0_index", torch.int32, (N,), q.device)
     rc = lib().gdn_chunk_fwd_indexed(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                      _ptr(cu_seqlens), _ptr(h0), int(h0.shape[0]), _ptr(h0_index), _ptr(o),
-                                     _ptr(hT), _stream(stream))
+                                     _ptr(hT), _stream(stream, q.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd_indexed")
     return o, hT
@@ -235,29 +246,29 @@ class ChunkPlan:
         _check(self.o, "o", torch.bfloat16, (T, Hv, D), dev)
         _check(self.hT, "hT", torch.float32, (N, Hv, D, D), dev)
         need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
-        self.workspace = workspace if workspace is not None and workspace.numel() >= need else \
-            torch.empty(need, dtype=torch.uint8, device=dev)
+        self.workspace = _workspace(workspace, need, dev)
+        self.device = dev
         self.desc = _desc(T, N, Hk, Hv, self.workspace.data_ptr(), self.workspace.numel())
         self.args = (q, k, v, g, beta, cu_seqlens, h0)
 
     def prep(self, stream=None):
         q, k, v, g, beta, cu, h0 = self.args
         rc = lib().gdn_chunk_prep(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu),
-                                  _stream(stream))
+                                  _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_chunk_prep")
 
     def state_pass(self, stream=None):
         q, k, v, g, beta, cu, h0 = self.args
         rc = lib().gdn_state_pass(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(h0),
-                                  _ptr(self.o), _ptr(self.hT), _stream(stream))
+                                  _ptr(self.o), _ptr(self.hT), _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_state_pass")
 
     def forward(self, stream=None):
         q, k, v, g, beta, cu, h0 = self.args
         rc = lib().gdn_chunk_fwd(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu),
-                                 _ptr(h0), _ptr(self.o), _ptr(self.hT), _stream(stream))
+                                 _ptr(h0), _ptr(self.o), _ptr(self.hT), _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_chunk_fwd")
 
@@ -320,17 +331,16 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
     need = gdn_mixer_fwd_workspace_size(T, N, Hk, Hv, 4, norm_eps)
     if need == 0:
         raise GdnError(GDN_ERR_SHAPE, "gdn_mixer_fwd_workspace_size")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     m = MixerDesc(_desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), 4, float(norm_eps))
     if cont:
         rc = lib().gdn_mixer_fwd_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
                                       _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(conv_in), S, _ptr(state_index),
-                                      _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream))
+                                      _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream, dev))
         where = "gdn_mixer_fwd_cont"
     else:
         rc = lib().gdn_mixer_fwd(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
-                                 _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream))
+                                 _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream, dev))
         where = "gdn_mixer_fwd"
     if rc != GDN_OK:
         raise GdnError(rc, where)

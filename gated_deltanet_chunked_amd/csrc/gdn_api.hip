@@ -36,13 +36,13 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-// Workgroups of the state pass that fit on the current device at once (one per CU: its LDS use
-// allows no more), rounded down to a multiple of 8; cached per device.
+// Workgroups of the state pass that fit at once on the device the stream runs on (one per CU:
+// its LDS use allows no more), rounded down to a multiple of 8; cached per device.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_max_groups[kMaxDevices];
-int device_max_groups() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+int device_max_groups(hipStream_t stream) {
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
   if (dev >= 0) {
     const int cached = g_max_groups[dev].load(std::memory_order_relaxed);
     if (cached > 0) return cached;
@@ -186,7 +186,7 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
   }
   if (stage & kPass) {
     gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T, s.N,
-                           s.Hk, s.Hv, device_max_groups(), stream);
+                           s.Hk, s.Hv, device_max_groups(stream), stream);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;

@@ -70,6 +70,22 @@ def test_determinism_and_dirty_workspace():
         assert np.array_equal(o_, outs[0][0]) and np.array_equal(h_, outs[0][1])
 
 
+def test_workspace_argument_checks():
+    say("[workspace] too small, wrong dtype")
+    x = gi.make_gdn_inputs(2, 4, [100], seed=62)
+    d = dev_inputs(x)
+    need = gdn.gdn_chunk_fwd_workspace_size(100, 1, 2, 4)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], None)
+    with pytest.raises(ValueError):
+        gdn.gdn_chunk_fwd(*args, workspace=torch.empty(need - 1, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        gdn.gdn_chunk_fwd(*args, workspace=torch.empty(need, dtype=torch.float32, device="cuda"))
+    o, _ = gdn.gdn_chunk_fwd(*args, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    o2, _ = gdn.gdn_chunk_fwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
 def test_changed_input_replay():
     say("[replay] same shape, inputs A, B, A")
     xa = gi.make_gdn_inputs(4, 8, [300], seed=60)
