@@ -18,12 +18,13 @@
 // state does not drift over hundreds of chunks; bf16 is used where only the output sees it.
 //
 // A chunk takes three phases, separated by workgroup barriers b1, b2, b3:
-//   phase 1: compute waves: K^T fragments, X = K H, R = V - e^G o X to LDS (hi/lo)
-//            output waves:  Q H                                                     -> b1
-//   phase 2: compute waves: U~ = T' R; U~ (decayed hi/lo and plain) to LDS           -> b2
-//   phase 3: compute waves: H update, bf16 H to LDS
-//            output waves:  o = e^G o (Q H) + P U~ into an LDS staging slot           -> b3
-// and the output waves store chunk c's rows at the start of chunk c + 1.
+//   phase 1: compute waves: X = K H, R = V - e^G o X to LDS (hi/lo)
+//            output waves:  o = e^G o (Q H) + P U~ of the previous chunk, staged in LDS -> b1
+//   phase 2: compute waves: U~ = T' R (K^T fragments read behind it); U~ (decayed
+//            hi/lo and plain) to LDS
+//            output waves:  the previous chunk's rows to memory; Q H                 -> b2
+//   phase 3: compute waves: H update, bf16 H to LDS                                  -> b3
+// so the output path of chunk c finishes during chunk c + 1, off the chunk's last barrier.
 // Thirteen waves per workgroup:
 //   * 4 compute waves (one per SIMD) keep the state and do no global access in the chunk loop.
 //   * 4 producer waves issue the bulk loads as global->LDS loads (global_load_lds_dwordx4: 1 KiB
@@ -357,24 +358,6 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
   const int lj = l & 15, lg = l >> 4;
   const unsigned char *kt = ts + kTK;
 
-  // K^T fragments for the state update, read transposed from the K tile: fragment (accumulator
-  // a, token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][state_key(w, a, lj)].
-  // ds_read_b64_tr_b16: within each 16-lane group, lane r names 4 consecutive bf16 (row r of a
-  // 16 x 4 matrix M) and lane i receives M[4 j + i / 4][i % 4], j = 0..3.  With lane r = 4 j + q
-  // naming K[token t + j][state_key(w, a, 4 q) .. + 3], lane i receives K[t .. t + 3] of key
-  // state_key(w, a, i): half a fragment (4 tokens) per read.
-  bf16x8 kc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int key = state_key(w, a, 4 * (lj & 3));
-      const int tok = 32 * ks + 8 * lg + (lj >> 2);
-      const v4i16 lo4 = lds_read_tr16(kt + swz(tok, key));
-      const v4i16 hi4 = lds_read_tr16(kt + swz(tok + 4, key));
-      kc[a][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-
   // X = K H (contraction over the 128 keys; B operand = bf16 H from LDS), in two chains
   f32x4 X = zero4(), X2 = zero4();
 #pragma unroll
@@ -410,13 +393,31 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
   }
   __syncthreads();
 
-  // U~ = T' R for row block w (3 hi/lo terms; row blocks 2, 3 need two token steps)
+  // U~ = T' R for row block w (3 hi/lo terms; row blocks 2, 3 need two token steps); the K^T
+  // fragments of phase 3 are read here, behind the T' and R reads.
+  bf16x8 kc[2][2];
   f32x4 U = zero4();
   {
     const unsigned char *tt = ts + kTT + frag_base(w) * kFragBytes + l * 16;
     const bf16x8 th = lds_bf16x8(tt), tl = lds_bf16x8(tt + kTpBytes / 2);
     const bf16x8 bh = lds_bf16x8(Rh + vmaj(lj, 8 * lg));
     const bf16x8 bl = lds_bf16x8(Rl + vmaj(lj, 8 * lg));
+    // K^T fragments for the state update, read transposed from the K tile: fragment (accumulator
+    // a, token step ks), lane (lj, lg) holds K[token 32 ks + 8 lg + e][state_key(w, a, lj)].
+    // ds_read_b64_tr_b16: within each 16-lane group, lane r names 4 consecutive bf16 (row r of a
+    // 16 x 4 matrix M) and lane i receives M[4 j + i / 4][i % 4], j = 0..3.  With lane r = 4 j + q
+    // naming K[token t + j][state_key(w, a, 4 q) .. + 3], lane i receives K[t .. t + 3] of key
+    // state_key(w, a, i): half a fragment (4 tokens) per read.
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int key = state_key(w, a, 4 * (lj & 3));
+        const int tok = 32 * ks + 8 * lg + (lj >> 2);
+        const v4i16 lo4 = lds_read_tr16(kt + swz(tok, key));
+        const v4i16 hi4 = lds_read_tr16(kt + swz(tok + 4, key));
+        kc[a][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     U = mfma_bf16(th, bh, U);
     U = mfma_bf16(th, bl, U);
     U = mfma_bf16(tl, bh, U);
