@@ -211,3 +211,23 @@ def test_many_sequences_persistent_pass():
     xg = gi.GdnInputs(x.q, x.k, x.v, x.beta, x.g, x.cu, gathered)
     og, hg = run_gpu(xg)
     assert np.array_equal(oi.float().cpu().numpy(), og) and np.array_equal(hi.cpu().numpy(), hg)
+
+
+def test_many_tiny_sequences():
+    # 600 sequences of 0-3 tokens with a few full chunks among them: 19,200 work items walked by
+    # the persistent grid, most of them one chunk (or none) long, so almost every step switches
+    # item.  Parity against the oracle, and bitwise equality of a few sequences run alone.
+    rng = np.random.default_rng(93)
+    lengths = [int(x) for x in rng.choice([0, 1, 2, 3, 64, 65], size=600, p=[0.2, 0.3, 0.2, 0.2, 0.05, 0.05])]
+    say(f"[tiny] {len(lengths)} sequences, {sum(lengths)} tokens, Hk=2 Hv=4")
+    x = gi.make_gdn_inputs(2, 4, lengths, seed=94, with_h0=True)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), "600 tiny sequences")
+    cu = x.cu
+    for n in (0, 1, 299, 599):
+        sl = slice(cu[n], cu[n + 1])
+        xs = gi.GdnInputs(x.q[sl], x.k[sl], x.v[sl], x.beta[sl], x.g[sl], np.array([0, lengths[n]], np.int32),
+                          x.h0[n:n + 1])
+        o1, h1 = run_gpu(xs)
+        assert np.array_equal(o[sl], o1) and np.array_equal(hT[n], h1[0]), f"sequence {n} differs"
+
