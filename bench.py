@@ -23,6 +23,7 @@ SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE.
 Workloads (seeded, synthetic; see gdn_inputs.py):
     t539_h16x32      single sequence, T=539, Hk=16, Hv=32, d=128  (default)
     t256_h4, varlen7_t677_h0, t3399_h16x32, t16384_h16x32
+    t16384_h2x4      T=16384 at Hk=2, Hv=4: one GPU's share when the heads are split over 8 GPUs
     mixer_t936_x48   48 GDN mixer layers at T=936, Hk=16, Hv=32, one layer per seed
 """
 from __future__ import annotations

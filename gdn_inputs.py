@@ -80,6 +80,8 @@ CASES = {
                                with_h0=True),
     "t3399_h16x32": GdnCase("t3399_h16x32", 16, 32, [3399], seed=4),
     "t16384_h16x32": GdnCase("t16384_h16x32", 16, 32, [16384], seed=5),
+    # one GPU's share of T = 16,384 when the 32 v-heads are split over 8 GPUs by heads
+    "t16384_h2x4": GdnCase("t16384_h2x4", 2, 4, [16384], seed=6),
 }
 
 
