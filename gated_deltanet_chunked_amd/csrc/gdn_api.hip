@@ -16,7 +16,9 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                        const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
-                       hipStream_t stream);
+                       hipStream_t stream, SplitPass sp);
+void launch_state_scan(const float *phi, const float *bend, const float *h0, const int32_t *h0_index,
+                       int num_h0, float *hs, int segs, int Hv, hipStream_t stream);
 void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
                             const int32_t *state_index, int num_states, const float *g,
                             const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
@@ -96,7 +98,9 @@ struct Shape {
   int64_t T;
   int N, Hk, Hv;
   int64_t nslots;
-  size_t rec_bytes;  // workspace of the chunk path: one record per (chunk slot, v-head)
+  size_t rec_bytes;    // one record per (chunk slot, v-head)
+  size_t split_bytes;  // state buffers of the time split (one sequence with few heads), or 0
+  size_t ws_bytes;     // workspace of the chunk path: records, then the split's buffers
 };
 
 int check_shape(const gdn_chunk_desc *d, Shape &s) {
@@ -115,6 +119,11 @@ int check_shape(const gdn_chunk_desc *d, Shape &s) {
   s.nslots = gdn::num_slots(s.T, s.N);
   if (s.nslots > INT32_MAX) return GDN_ERR_SHAPE;
   s.rec_bytes = round_up((size_t)s.nslots * s.Hv * gdn::kRecBytes);
+  // A single sequence of at least 32 chunks with at most 8 v-heads may be cut along time into 4 or
+  // more segments (plan_split); its three state buffers hold kSplitStates states each.
+  s.split_bytes = (s.N == 1 && 4 * s.Hv <= gdn::kSplitStates && s.T > 31 * gdn::kChunk)
+                      ? 3 * (size_t)gdn::kSplitStates * gdn::kDim * gdn::kDim * 4 : 0;
+  s.ws_bytes = s.rec_bytes + s.split_bytes;
   return GDN_OK;
 }
 
@@ -148,7 +157,7 @@ int check_chunk_args(const gdn_chunk_desc *d, Shape &s, Stage stage, const void 
   if (tok && pass && (!v || !o)) return GDN_ERR_NULL;
   if (pool.index && pool.rows < 1) return GDN_ERR_SHAPE;
   if (!pool.index) pool.rows = s.N;
-  const size_t need = s.rec_bytes;
+  const size_t need = s.ws_bytes;
   if (!d->workspace || d->workspace_bytes < need) return GDN_ERR_WORKSPACE;
   if (!prep) g = beta = nullptr;
   if (!pass) v = nullptr, pool = StatePool{nullptr, s.N, nullptr}, o = nullptr, hT = nullptr;
@@ -173,6 +182,26 @@ int check_chunk_args(const gdn_chunk_desc *d, Shape &s, Stage stage, const void 
   return check_alias(outs, ins, ok);
 }
 
+// The time split: one sequence of nc chunks whose Hv x 8 work items leave most of the device idle
+// is cut into segs segments of m chunks (segs x Hv x 8 <= the device's workgroups, segs x Hv <=
+// kSplitStates, at least 8 chunks a segment).  The state pass then runs three times over all
+// segments at once -- end states from zero states, transitions (v = 0 from the identity), and the
+// outputs from each segment's true initial state -- with a scan of the states in between, instead
+// of once over nc chunks on a few CUs: about 3 / segs of the chunk steps.  It is planned only with
+// at least 4 segments; otherwise segs is 0 and the pass runs as usual.
+gdn::SplitPass plan_split(const Shape &s, int max_groups) {
+  gdn::SplitPass sp{0, 0, 0, nullptr, nullptr};
+  if (!s.split_bytes || s.T <= 0) return sp;
+  const int nc = (int)((s.T + gdn::kChunk - 1) / gdn::kChunk);
+  int segs = max_groups / (s.Hv * gdn::kDvTiles);
+  segs = segs < gdn::kSplitStates / s.Hv ? segs : gdn::kSplitStates / s.Hv;
+  segs = segs < nc / 8 ? segs : nc / 8;
+  if (segs < 4) return sp;
+  sp.m = (nc + segs - 1) / segs;
+  sp.segs = (nc + sp.m - 1) / sp.m;
+  return sp;
+}
+
 // Enqueues the checked stages.
 int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const void *v,
               const float *g, const float *beta, const int32_t *cu, const StatePool &pool, void *o,
@@ -185,8 +214,31 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
     if (e != hipSuccess) return record_hip(e);
   }
   if (stage & kPass) {
-    gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T, s.N,
-                           s.Hk, s.Hv, device_max_groups(stream), stream);
+    const int groups = device_max_groups(stream);
+    gdn::SplitPass sp = plan_split(s, groups);
+    if (sp.segs) {
+      // workspace after the records: end states | transitions | initial states of the segments
+      float *bend = reinterpret_cast<float *>(rec + s.rec_bytes);
+      float *phi = bend + (size_t)gdn::kSplitStates * gdn::kDim * gdn::kDim;
+      float *hs = phi + (size_t)gdn::kSplitStates * gdn::kDim * gdn::kDim;
+      sp.mode = 0;
+      sp.h_out = bend;
+      gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk, s.Hv,
+                             groups, stream, sp);
+      sp.mode = 1;
+      sp.h_out = phi;
+      gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk, s.Hv,
+                             groups, stream, sp);
+      gdn::launch_state_scan(phi, bend, pool.h0, pool.index, pool.rows, hs, sp.segs, s.Hv, stream);
+      sp.mode = 2;
+      sp.h_in = hs;
+      sp.h_out = nullptr;
+      gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, hT, rec, s.T, s.N, s.Hk, s.Hv, groups,
+                             stream, sp);
+    } else {
+      gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T, s.N, s.Hk,
+                             s.Hv, groups, stream, sp);
+    }
     return record_hip(hipGetLastError());
   }
   return GDN_OK;
@@ -217,7 +269,7 @@ int gdn_last_hip_error(void) { return g_last_hip_error; }
 size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d) {
   Shape s;
   if (check_shape(d, s) != GDN_OK) return 0;
-  return s.rec_bytes;
+  return s.ws_bytes;
 }
 
 int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
@@ -286,7 +338,7 @@ int mixer_layout(const gdn_mixer_desc *d, MixerLayout &m) {
   if (!(d->norm_eps > 0.f)) return GDN_ERR_UNSUPPORTED;
   if (2 * (int64_t)m.s.Hk + m.s.Hv > 65535) return GDN_ERR_SHAPE;  // head segments on grid y
   if ((m.s.T * m.s.Hv + 15) / 16 > INT32_MAX) return GDN_ERR_SHAPE;  // gated RMSNorm grid x
-  m.chunk_bytes = m.s.rec_bytes;
+  m.chunk_bytes = m.s.ws_bytes;
   m.q_bytes = round_up((size_t)m.s.T * m.s.Hk * gdn::kDim * 2);
   m.v_bytes = round_up((size_t)m.s.T * m.s.Hv * gdn::kDim * 2);
   m.total = m.chunk_bytes + 2 * m.q_bytes + 2 * m.v_bytes;

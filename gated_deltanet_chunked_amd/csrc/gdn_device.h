@@ -45,6 +45,20 @@ constexpr int kRecBytes = kRecED + kChunk * 4;            // 18944
 __host__ __device__ constexpr int frag_row_block(int f) { return f < 2 ? f : (f < 4 ? 2 : 3); }
 __host__ __device__ constexpr int frag_k_step(int f) { return (f == 3 || f == 5) ? 1 : 0; }
 
+// One pass of the time split of a single long sequence (segs > 0): the sequence's chunks are cut
+// into segments of m chunks, and grid "sequence" n is segment n.  mode 0: each segment from a
+// zero state, end states to h_out, o not written; mode 1: v taken as zero and the identity as
+// initial state, so the end state is the segment's transition matrix, to h_out, o not written;
+// mode 2: each segment from h_in[n], o written, the last segment's end state to hT.  h_in and h_out
+// are [segs, Hv, 128, 128] fp32, key-major.
+struct SplitPass {
+  int segs, m, mode;
+  const float *h_in;
+  float *h_out;
+};
+// With a split, the state buffers hold at most kSplitStates (segment, v-head) states each.
+constexpr int kSplitStates = 32;
+
 // Chunk-slot numbering: chunk c of sequence n lives in slot cu[n] / 64 + n + c.  The map is
 // injective and monotone, and every slot index is below T / 64 + N.
 __host__ __device__ inline int64_t num_slots(int64_t T, int32_t N) { return T / kChunk + N; }

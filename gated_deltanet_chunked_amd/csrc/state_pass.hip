@@ -354,7 +354,7 @@ template <bool kWriteHt>
 __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *ds, int w,
                                            int l, f32x4 (&H)[2], unsigned char *Ht,
                                            unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
-                                           unsigned char *Ul, unsigned char *Uo) {
+                                           unsigned char *Ul, unsigned char *Uo, bool zero_v = false) {
   const int lj = l & 15, lg = l >> 4;
   const unsigned char *kt = ts + kTK;
 
@@ -377,7 +377,7 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
   {
     const v4i16 v4 = lds_read_tr16(ts + kTV + ((16 * w + 4 * lg + (lj >> 2)) * kDvTile + 4 * (lj & 3)) * 2);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) vv[rr] = bits_to_float((unsigned short)v4[rr]);
+    for (int rr = 0; rr < 4; ++rr) vv[rr] = zero_v ? 0.f : bits_to_float((unsigned short)v4[rr]);
   }
 
   // R = V - e^G o X (hi/lo to LDS, value-major)
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const float *h0, const int32_t *__restrict__ h0_index, int num_h0,
     unsigned short *__restrict__ o, float *hT,  // hT may equal h0 when h0_index is NULL
-    const uint8_t *__restrict__ rec, int Hk, int Hv) {
+    const uint8_t *__restrict__ rec, int Hk, int Hv, SplitPass sp) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
@@ -618,10 +618,20 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   const int d0 = kDvTile * tile;
   const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int tb = cu[n], te = cu[n + 1];
+  // n is a sequence, or with a time split a segment of sequence 0 (m chunks from chunk m n on)
+  int tb, te, slot0;
+  if (sp.segs) {
+    tb = min(cu[0] + kChunk * sp.m * n, cu[1]);
+    te = min(tb + kChunk * sp.m, cu[1]);
+    slot0 = cu[0] / kChunk + sp.m * n;
+  } else {
+    tb = cu[n];
+    te = cu[n + 1];
+    slot0 = tb / kChunk + n;
+  }
   const int nc = (te - tb + kChunk - 1) / kChunk;
-  const int slot0 = tb / kChunk + n;
   const size_t state_base = ((size_t)n * Hv + h) * kDim * kDim;
+  const bool write_o = !sp.segs || sp.mode == 2;
 
   if (w == kPrefetchWave) {
     // Prefetch wave: warms L2 kPrefetchAhead chunks ahead of use and never waits for its loads
@@ -680,14 +690,14 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
           load_p(pf, rec_at(rec, slot0 + c, h, Hv), ow, l);
         }
         __syncthreads();  // b1
-        if (c > 0) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+        if (c > 0 && write_o) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
         O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
         __syncthreads();  // b3
       }
       out_stage(O, pf, decs + ((nc - 1) % kDecStages) * kDecBytes, Uo + ((nc - 1) & 1) * kXBytes, ow, l,
                 oslot);
-      store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+      if (write_o) store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
     }
     return;
   }
@@ -745,17 +755,20 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   // State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].  Sequence n starts
   // from initial state h0_index[n] of the pool (zeros outside [0, num_h0)), or from state n.
   const float *h0s = nullptr;
-  if (h0) {
+  if (sp.segs) {
+    if (sp.mode == 2) h0s = sp.h_in + state_base;
+  } else if (h0) {
     const int r = h0_index ? h0_index[n] : n;
     if (r >= 0 && r < num_h0) h0s = h0 + ((size_t)r * Hv + h) * kDim * kDim;
   }
+  const bool ident = sp.segs && sp.mode == 1;
   f32x4 H[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int key = state_key(w, a, 4 * lg + rr);
-      H[a][rr] = h0s ? h0s[(size_t)key * kDim + d0 + lj] : 0.f;
+      H[a][rr] = h0s ? h0s[(size_t)key * kDim + d0 + lj] : (ident && key == d0 + lj ? 1.f : 0.f);
     }
 
   if (nc > 0) {
@@ -764,18 +777,32 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
                   pack_bf16x2(H[a][2], H[a][3]));
     __syncthreads();
-    for (int c = 0; c < nc; ++c)
-      chunk_step<true>(tiles + (c % kTileStages) * kTileBytes, decs + (c % kDecStages) * kDecBytes, w,
-                       l, H, Ht, Rh, Rl, Uh, Ul, Uo + (c & 1) * kXBytes);
+    // Unrolled over the period of the ring slots and the U~ buffers (3 x 2), so every slot address
+    // is a compile-time offset rather than per-chunk address arithmetic on the compute waves.
+    for (int c0 = 0; c0 < nc; c0 += 6) {
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        if (c0 + u < nc)
+          chunk_step<true>(tiles + (u % kTileStages) * kTileBytes, decs + (u % kDecStages) * kDecBytes, w,
+                           l, H, Ht, Rh, Rl, Uh, Ul, Uo + (u & 1) * kXBytes, ident);
+      }
+    }
   }
 
-  if (hT) {
+  float *hdst = hT ? hT + state_base : nullptr;
+  if (sp.segs)
+    hdst = sp.mode < 2 ? sp.h_out + state_base
+                       : (n == sp.segs - 1 && hT ? hT + (size_t)h * kDim * kDim : nullptr);
+  if (hdst) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int key = state_key(w, a, 4 * lg + rr);
-        __builtin_nontemporal_store(H[a][rr], hT + state_base + (size_t)key * kDim + d0 + lj);
+        if (sp.segs && sp.mode < 2)
+          hdst[(size_t)key * kDim + d0 + lj] = H[a][rr];  // read by the next kernel: keep it cached
+        else
+          __builtin_nontemporal_store(H[a][rr], hdst + (size_t)key * kDim + d0 + lj);
       }
   }
 }
@@ -977,13 +1004,94 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   }
 }
 
+// Initial states of the segments of a time-split sequence: hs[0] is the sequence's own initial
+// state (h0 row h0_index[0], or row 0, or zeros), and hs[s] = phi[s-1] hs[s-1] + bend[s-1] for
+// s = 1 .. segs - 1 -- a segment maps its initial state H to phi H + bend (states key-major, so the
+// transition multiplies from the left).  fp32 on the matrix cores (v_mfma_f32_16x16x4_f32, exact
+// products).  One workgroup per (v-head, 16-column tile), 8 waves; wave wv makes output rows
+// 16 wv .. 16 wv + 15, the previous state's tile stays in LDS.
+constexpr int kScanThreads = 512;
+__global__ __launch_bounds__(kScanThreads) void state_scan_kernel(
+    const float *__restrict__ phi, const float *__restrict__ bend, const float *h0,
+    const int32_t *__restrict__ h0_index, int num_h0, float *__restrict__ hs, int segs, int Hv) {
+  // [key][column] of the previous segment's initial state; key k sits at row hp_row(k), which
+  // rotates each aligned group of 4 keys by k / 32, so the four lane groups' reads of keys
+  // 32 lg + i fall on different banks.
+  __shared__ float Hp[kDim * kDvTile];
+  auto hp_row = [](int k) { return (k & ~3) | ((k + (k >> 5)) & 3); };
+  const int tile = blockIdx.x % kDvTiles, h = blockIdx.x / kDvTiles, d0 = kDvTile * tile;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, lj = l & 15, lg = l >> 4;
+  const size_t hb = (size_t)h * kDim * kDim, seg = (size_t)Hv * kDim * kDim;
+  const float *h0s = nullptr;
+  if (h0) {
+    const int r = h0_index ? h0_index[0] : 0;
+    if (r >= 0 && r < num_h0) h0s = h0 + ((size_t)r * Hv + h) * kDim * kDim;
+  }
+  for (int e = tid; e < kDim * kDvTile; e += kScanThreads) {
+    const int key = e / kDvTile, col = e % kDvTile;
+    const float x = h0s ? h0s[(size_t)key * kDim + d0 + col] : 0.f;
+    Hp[hp_row(key) * kDvTile + col] = x;
+    hs[hb + (size_t)key * kDim + d0 + col] = x;
+  }
+  __syncthreads();
+  // Product i takes contraction index k = 32 lg + i in lane group lg, so a lane's A operands are 32
+  // consecutive floats of its row (eight 16-byte loads).  Two register sets alternate: step s + 2's
+  // operands are loaded into the set step s has just used, before step s's results are stored
+  // (one counter tracks loads and stores in order, so a load issued after a store would wait
+  // for the store).  The 32 products run as two independent chains.
+  auto load_step = [&](int s, f32x4 (&a4)[kDim / 16], f32x4 &b4) {
+    const float *P = phi + (size_t)(s - 1) * seg + hb + (size_t)(16 * wv + lj) * kDim + 32 * lg;
+    const float *B = bend + (size_t)(s - 1) * seg + hb;
+#pragma unroll
+    for (int i = 0; i < kDim / 16; ++i) a4[i] = *reinterpret_cast<const f32x4 *>(P + 4 * i);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b4[r] = B[(size_t)(16 * wv + 4 * lg + r) * kDim + d0 + lj];
+  };
+  auto step = [&](int s, f32x4 (&a4)[kDim / 16], f32x4 &b4) {
+    float hv[kDim / 4];  // B operands, all read before the first product
+#pragma unroll
+    for (int i = 0; i < kDim / 4; ++i) hv[i] = Hp[hp_row(32 * lg + i) * kDvTile + lj];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc0 = b4, acc1 = zero4();
+#pragma unroll
+    for (int i = 0; i < kDim / 4; i += 2) {
+      acc0 = mfma_f32(a4[i / 4][i % 4], hv[i], acc0);
+      acc1 = mfma_f32(a4[i / 4][i % 4 + 1], hv[i + 1], acc1);
+    }
+    const f32x4 acc = acc0 + acc1;
+    __syncthreads();  // every wave has read Hp
+    if (s + 2 < segs) load_step(s + 2, a4, b4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * wv + 4 * lg + r;
+      Hp[hp_row(key) * kDvTile + lj] = acc[r];
+      hs[(size_t)s * seg + hb + (size_t)key * kDim + d0 + lj] = acc[r];
+    }
+    __syncthreads();
+  };
+  f32x4 aA[kDim / 16], bA, aB[kDim / 16], bB;
+  if (segs > 1) load_step(1, aA, bA);
+  if (segs > 2) load_step(2, aB, bB);
+  for (int s = 1; s < segs; s += 2) {
+    step(s, aA, bA);
+    if (s + 1 >= segs) break;
+    step(s + 1, aB, bB);
+  }
+}
+
+void launch_state_scan(const float *phi, const float *bend, const float *h0, const int32_t *h0_index,
+                       int num_h0, float *hs, int segs, int Hv, hipStream_t stream) {
+  hipLaunchKernelGGL(state_scan_kernel, dim3(Hv * kDvTiles), dim3(kScanThreads), 0, stream, phi, bend,
+                     h0, h0_index, num_h0, hs, segs, Hv);
+}
+
 void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                        const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                        const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
-                       hipStream_t stream) {
+                       hipStream_t stream, SplitPass sp) {
   // Items: N Hv 8 (a multiple of 8).  One round when they fit on the device at one workgroup per
   // CU (max_groups, a multiple of 8), else max_groups persistent workgroups.
-  const int total = N * Hv * kDvTiles;
+  const int total = (sp.segs ? sp.segs : N) * Hv * kDvTiles;
   const int G = total <= max_groups ? total : max_groups;
   const bool o_nt = (uint64_t)T * (uint64_t)Hv * kDim * 2 <= kOStreamBytes;
   const unsigned short *q16 = static_cast<const unsigned short *>(q);
@@ -994,7 +1102,7 @@ void launch_state_pass(const void *q, const void *k, const void *v, const int32_
   if (G == total)
     hipLaunchKernelGGL(o_nt ? state_pass_kernel<true> : state_pass_kernel<false>, dim3(G),
                        dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0, o16, hT,
-                       r8, Hk, Hv);
+                       r8, Hk, Hv, sp);
   else
     hipLaunchKernelGGL(o_nt ? state_pass_multi_kernel<true> : state_pass_multi_kernel<false>,
                        dim3(G), dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0,

@@ -47,13 +47,17 @@ def test_abi_version_and_status_strings():
 
 
 def test_workspace_size():
-    # slots = T // 64 + N; per slot: Hv records of 18944 B (256-aligned)
+    # slots = T // 64 + N; per slot: Hv records of 18944 B (256-aligned); a single sequence of at
+    # least 32 chunks with at most 8 v-heads adds three buffers of 32 fp32 128 x 128 states (the
+    # time split)
     def expect(T, N, Hk, Hv):
         r = lambda x: (x + 255) // 256 * 256
         s = T // 64 + N
-        return r(s * Hv * 18944)
-    for args in [(16384, 1, 16, 32), (677, 7, 16, 32), (0, 1, 4, 4), (1, 3, 1, 2)]:
-        assert gdn.gdn_chunk_fwd_workspace_size(*args) == expect(*args)
+        split = 3 * 32 * 128 * 128 * 4 if (N == 1 and Hv <= 8 and T > 31 * 64) else 0
+        return r(s * Hv * 18944) + split
+    for args in [(16384, 1, 16, 32), (677, 7, 16, 32), (0, 1, 4, 4), (1, 3, 1, 2), (16384, 1, 2, 4),
+                 (1984, 1, 1, 8), (1985, 1, 1, 8), (1985, 1, 1, 16), (1985, 2, 1, 8)]:
+        assert gdn.gdn_chunk_fwd_workspace_size(*args) == expect(*args), args
     assert gdn.gdn_chunk_fwd_workspace_size(10, 1, 3, 4) == 0     # Hv % Hk != 0
     assert gdn.gdn_chunk_fwd_workspace_size(10, 0, 1, 1) == 0     # N < 1
     assert gdn.gdn_chunk_fwd_workspace_size(-1, 1, 1, 1) == 0     # T < 0
