@@ -92,7 +92,8 @@ GDN_EXPORT const char *gdn_status_string(int status);
 GDN_EXPORT int gdn_last_hip_error(void);
 
 /* Workspace bytes gdn_chunk_fwd needs for this shape; 0 if the description is invalid.
- * The workspace and pointer fields of *d are ignored. */
+ * The workspace and pointer fields of *d are ignored.  One sequence (N = 1) of at least 32 chunks
+ * with at most 8 v-heads needs 6 MiB more: its state pass may run split along time (below). */
 GDN_EXPORT size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d);
 
 /*
@@ -103,7 +104,10 @@ GDN_EXPORT size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d);
  *   hT : final states, or NULL to skip them (device); may equal h0
  * Computes in 64-token chunks: per chunk a local cumsum of g, the K K^T / (I + A)^-1 UT
  * transform, a sequential inter-chunk state pass with fp32 state, and the chunk output
- * ("open-jev-fast" README, "Phase 3" item 1, names these steps).
+ * ("open-jev-fast" README, "Phase 3" item 1, names these steps).  A single sequence whose heads
+ * would leave most of the device idle has its state pass split along time (segment end states,
+ * segment transitions, a scan of the segment states, then the outputs); the results meet the same
+ * tolerances, and are not bitwise those of a call on a different batch shape.
  */
 GDN_EXPORT int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
                   const float *g, const float *beta, const int32_t *cu_seqlens, const float *h0,
