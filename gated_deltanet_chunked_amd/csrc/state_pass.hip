@@ -1015,10 +1015,10 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(
     const float *__restrict__ phi, const float *__restrict__ bend, const float *h0,
     const int32_t *__restrict__ h0_index, int num_h0, float *__restrict__ hs, int segs, int Hv) {
   // [key][column] of the previous segment's initial state; key k sits at row hp_row(k), which
-  // rotates each aligned group of 4 keys by k / 32, so the four lane groups' reads of keys
-  // 32 lg + i fall on different banks.
+  // rotates each aligned group of 4 keys by k / 4, so the four lane groups' reads of keys
+  // 16 j + 4 lg + e fall on different banks.
   __shared__ float Hp[kDim * kDvTile];
-  auto hp_row = [](int k) { return (k & ~3) | ((k + (k >> 5)) & 3); };
+  auto hp_row = [](int k) { return (k & ~3) | ((k + (k >> 2)) & 3); };
   const int tile = blockIdx.x % kDvTiles, h = blockIdx.x / kDvTiles, d0 = kDvTile * tile;
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, lj = l & 15, lg = l >> 4;
   const size_t hb = (size_t)h * kDim * kDim, seg = (size_t)Hv * kDim * kDim;
@@ -1034,23 +1034,24 @@ __global__ __launch_bounds__(kScanThreads) void state_scan_kernel(
     hs[hb + (size_t)key * kDim + d0 + col] = x;
   }
   __syncthreads();
-  // Product i takes contraction index k = 32 lg + i in lane group lg, so a lane's A operands are 32
-  // consecutive floats of its row (eight 16-byte loads).  Two register sets alternate: step s + 2's
+  // Product p = 4 j + e takes contraction index k = 16 j + 4 lg + e in lane group lg: load j of a
+  // lane is 16 bytes of its row, and the four lane groups' loads j cover 64 contiguous bytes of
+  // each row, so one load instruction touches 16 cache lines instead of 64.  Two register sets alternate: step s + 2's
   // operands are loaded into the set step s has just used, before step s's results are stored
   // (one counter tracks loads and stores in order, so a load issued after a store would wait
   // for the store).  The 32 products run as two independent chains.
   auto load_step = [&](int s, f32x4 (&a4)[kDim / 16], f32x4 &b4) {
-    const float *P = phi + (size_t)(s - 1) * seg + hb + (size_t)(16 * wv + lj) * kDim + 32 * lg;
+    const float *P = phi + (size_t)(s - 1) * seg + hb + (size_t)(16 * wv + lj) * kDim + 4 * lg;
     const float *B = bend + (size_t)(s - 1) * seg + hb;
 #pragma unroll
-    for (int i = 0; i < kDim / 16; ++i) a4[i] = *reinterpret_cast<const f32x4 *>(P + 4 * i);
+    for (int i = 0; i < kDim / 16; ++i) a4[i] = *reinterpret_cast<const f32x4 *>(P + 16 * i);
 #pragma unroll
     for (int r = 0; r < 4; ++r) b4[r] = B[(size_t)(16 * wv + 4 * lg + r) * kDim + d0 + lj];
   };
   auto step = [&](int s, f32x4 (&a4)[kDim / 16], f32x4 &b4) {
     float hv[kDim / 4];  // B operands, all read before the first product
 #pragma unroll
-    for (int i = 0; i < kDim / 4; ++i) hv[i] = Hp[hp_row(32 * lg + i) * kDvTile + lj];
+    for (int i = 0; i < kDim / 4; ++i) hv[i] = Hp[hp_row(16 * (i >> 2) + 4 * lg + (i & 3)) * kDvTile + lj];
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc0 = b4, acc1 = zero4();
 #pragma unroll
