@@ -1,21 +1,23 @@
 // state_pass.hip -- the sequential inter-chunk state pass fused with the chunk output.
 //
-// The "open-jev-fast" README ("Phase 3", item 1) keeps the fp32 recurrent state in registers and
-// passes only the state from chunk to chunk.  Here one workgroup owns one (sequence, v-head,
+// As in the fused kernel of the "open-jev-fast" README ("Phase 3", item 1), the fp32 recurrent
+// state stays on chip and is all that one chunk hands to the next.  Here one workgroup owns one (sequence, v-head,
 // 16-column slice of the 128 value columns): the state slice H[:, cols] (128 x 16 fp32) lives in
 // MFMA accumulators, spread over 4 compute waves (32 key rows each, see state_key), and the
 // chunks of the sequence are walked in order.  Sequences, heads and slices run in parallel.
 //
 // With H = S^T (key-major), local cumsum G, T' = (I + A)^-1 diag(beta) and
 // P = tril(Q K^T o e^{G_i - G_j}) from chunk_prep.hip, one chunk is
-//     X  = K H                                   (bf16 K x bf16 H, fp32 accumulate)
+//     X  = K H                                   (bf16 K x H split hi/lo: 2 MFMA terms)
 //     R  = V - e^{G} o X
 //     U~ = T' R                                  (T' and R split hi/lo: 3 MFMA terms)
 //     o  = e^{G} o (Q H) + P U~                  (output path in plain bf16)
 //     H  = e^{G_last} H + K^T (e^{G_last - G} o U~)   (decayed U~ split hi/lo: 2 MFMA terms)
 // which is the chunked form of the gated delta rule: (I + A) U~ = diag(beta)(V - e^G o K H).
 // The hi/lo splits keep the state path at about 16 significant bits per operand, so the fp32
-// state does not drift over hundreds of chunks; bf16 is used where only the output sees it.
+// state does not drift over hundreds of chunks even when nothing decays (g = 0, where a bf16 H in
+// X alone puts the final state 1.2e-3 off after 256 chunks); bf16 is used where only the output
+// sees it (H in Q H, P, U~ in P U~).
 //
 // A chunk takes three phases, separated by workgroup barriers b1, b2, b3:
 //   phase 1: compute waves: X = K H, R = V - e^G o X to LDS (hi/lo)
@@ -23,7 +25,7 @@
 //   phase 2: compute waves: U~ = T' R (K^T fragments read behind it); U~ (decayed
 //            hi/lo and plain) to LDS
 //            output waves:  the previous chunk's rows to memory; Q H                 -> b2
-//   phase 3: compute waves: H update, bf16 H to LDS                                  -> b3
+//   phase 3: compute waves: H update, H (bf16 hi and lo) to LDS                      -> b3
 // so the output path of chunk c finishes during chunk c + 1, off the chunk's last barrier.
 // Thirteen waves per workgroup:
 //   * 4 compute waves (one per SIMD) keep the state and do no global access in the chunk loop.
@@ -38,14 +40,14 @@
 //     never queue behind its own loads.
 //   * 1 prefetch wave pulls every line into L2 six chunks ahead of use, with loads it never waits
 //     for, since a miss to HBM takes longer than a chunk.
-// LDS carries the tiles and the three cross-wave exchanges per chunk: bf16 H, R and U~.
+// LDS carries the tiles and the three cross-wave exchanges per chunk: H, R and U~.
 #include "gdn_device.h"
 
 namespace gdn {
 
 namespace {
 
-constexpr int kHtBytes = kDvTile * kDim * 2;    // bf16 H exchange buffer
+constexpr int kHtBytes = kDvTile * kDim * 2;    // H exchange buffer (bf16 hi, and again lo)
 constexpr int kXBytes = kDvTile * kChunk * 2;    // R / U~ exchange buffers
 constexpr int kComputeWaves = 4;
 constexpr int kProducerWaves = 4;     // one per SIMD, beside one compute wave
@@ -98,24 +100,35 @@ __device__ __forceinline__ int state_key(int w, int a, int i) {
   return 8 * (w + 8 * a + 4 * (i >> 3)) + (i & 7);
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane (M0 holds the wave's
-// LDS base).  Completion is tracked by this wave's vmcnt only.
-__device__ __forceinline__ void dma16(const void *src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset, so that
-// moving to the next chunk costs scalar adds only.
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane (buffer_load_dwordx4
+// ... lds): a wave-uniform base in a buffer resource (SGPRs) and a 32-bit per-lane byte offset, so
+// that moving to the next chunk costs scalar work only.  The compiler's builtins set M0 (the LDS
+// base) themselves.  Completion is tracked by this wave's vmcnt only.  Offsets stay below 2^32
+// (at most 63 rows of a 16.7 MB row stride); the resource's range (2^32 - 1 bytes) never clips.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-               : "memory");
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(sbase), 0, 0xffffffffu, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(uintptr_t)lds, 16, voff, 0, 0, 0);
 }
 // 4 bytes per lane into a scratch LDS word: pulls the 128-byte line holding src into L2.
 __device__ __forceinline__ void touch(const void *src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory");
+  __builtin_amdgcn_global_load_lds((global_void *)(uintptr_t)src, (lds_void *)(uintptr_t)lds, 4, 0, 0);
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for the waves that issue global->LDS loads (producers, prefetch wave).  The
+// compiler sees those loads as outstanding LDS writes, and the workgroup release fence of
+// __syncthreads() would make it wait for all of them at every barrier, draining the tile ring.
+// These waves publish nothing at a barrier except what their explicit vmcnt waits have already
+// made land, so they take the barrier alone, fenced only against compiler reordering.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -319,8 +332,8 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
 // its own global->LDS loads still in flight, which would tie these reads to load latency.  out_qh
 // runs between b1 and b2: Q H needs the chunk's entry state, which the compute waves overwrite in
 // phase 3, and the Q tile's slot is not refilled before chunk c + 1.  out_stage runs once U~ is in
-// LDS, after the chunk's last barrier and before b1 of the next chunk (U~ alternates between two
-// buffers): it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg .. + 3
+// LDS, after the chunk's last barrier and before b1 of the next chunk (the compute waves rewrite
+// U~ only after that b1, so one buffer serves): it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg .. + 3
 // of column lj at byte 8 l); they are read back transposed and stored between b1 and b2 of the
 // next chunk (store_o).
 __device__ __forceinline__ f32x4 out_qh(const unsigned char *qt, const unsigned char *Ht, int w, int l) {
@@ -344,6 +357,22 @@ __device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const unsign
   store_u32x2(oslot + 8 * l, pack_bf16x2(O[0], O[1]), pack_bf16x2(O[2], O[3]));
 }
 
+// This wave's state slice into the H exchange buffers as bf16 hi (Ht) and lo (Htl = bf16(H - hi)):
+// the B operands of X = K H (hi and lo) and Q H (hi only) in the next chunk.
+__device__ __forceinline__ void write_ht(unsigned char *Ht, unsigned char *Htl, const f32x4 (&H)[2],
+                                         int w, int l) {
+  const int lj = l & 15, lg = l >> 4;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    uint32_t h0, l0, h1, l1;
+    split_pair(H[a][0], H[a][1], h0, l0);
+    split_pair(H[a][2], H[a][3], h1, l1);
+    const int off = vmaj(lj, state_key(w, a, 4 * lg));
+    store_u32x2(Ht + off, h0, h1);
+    store_u32x2(Htl + off, l0, l1);
+  }
+}
+
 // One chunk on compute wave w: tile ring slot ts (K, Q, V tiles and T' fragments), decay ring
 // slot ds.  Rows past the sequence end hold clamped data; they need no masking because T' has
 // zero rows and columns there (beta = 0), so U~ is zero on them, and their output rows are never
@@ -353,19 +382,22 @@ __device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const unsign
 template <bool kWriteHt>
 __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *ds, int w,
                                            int l, f32x4 (&H)[2], unsigned char *Ht,
-                                           unsigned char *Rh, unsigned char *Rl, unsigned char *Uh,
-                                           unsigned char *Ul, unsigned char *Uo, bool zero_v = false) {
+                                           unsigned char *Htl, unsigned char *Rh, unsigned char *Rl,
+                                           unsigned char *Uh, unsigned char *Ul, unsigned char *Uo,
+                                           bool zero_v = false) {
   const int lj = l & 15, lg = l >> 4;
   const unsigned char *kt = ts + kTK;
 
-  // X = K H (contraction over the 128 keys; B operand = bf16 H from LDS), in two chains
+  // X = K H (contraction over the 128 keys; B operands = H hi and lo from LDS), in two chains
   f32x4 X = zero4(), X2 = zero4();
 #pragma unroll
-  for (int ks = 0; ks < 4; ks += 2) {
-    X = mfma_bf16(lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 8 * lg)),
-                  lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), X);
-    X2 = mfma_bf16(lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 32 + 8 * lg)),
-                   lds_bf16x8(Ht + vmaj(lj, 32 * ks + 32 + 8 * lg)), X2);
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 a0 = lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 8 * lg));
+    const bf16x8 a1 = lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 64 + 8 * lg));
+    X = mfma_bf16(a0, lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), X);
+    X2 = mfma_bf16(a1, lds_bf16x8(Ht + vmaj(lj, 32 * ks + 64 + 8 * lg)), X2);
+    X = mfma_bf16(a0, lds_bf16x8(Htl + vmaj(lj, 32 * ks + 8 * lg)), X);
+    X2 = mfma_bf16(a1, lds_bf16x8(Htl + vmaj(lj, 32 * ks + 64 + 8 * lg)), X2);
   }
   X += X2;
   const f32x4 eg = *reinterpret_cast<const f32x4 *>(ds + kDecEG + (16 * w + 4 * lg) * 4);
@@ -454,22 +486,9 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
     }
   }
   if constexpr (kWriteHt) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-      store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
-                  pack_bf16x2(H[a][2], H[a][3]));
+    write_ht(Ht, Htl, H, w, l);
     __syncthreads();  // b3
   }
-}
-
-// bf16 copy of this wave's state slice into the H exchange buffer (the B operand of X = K H and
-// Q H in the next chunk).
-__device__ __forceinline__ void write_ht(unsigned char *Ht, const f32x4 (&H)[2], int w, int l) {
-  const int lj = l & 15, lg = l >> 4;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-    store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
-                pack_bf16x2(H[a][2], H[a][3]));
 }
 
 // ---- Work items --------------------------------------------------------------------------------
@@ -602,11 +621,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Htl[kHtBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Rh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Uh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ul[kXBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char Uo[2 * kXBytes];  // chunk c in Uo[c % 2]
+  __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
   __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
 
@@ -646,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       // pointers of chunk 2
 #pragma unroll
       for (int j = 0; j < 2; ++j) pf.ptr[j] += 2 * (size_t)pf.adv[j];
-      __syncthreads();
+      dma_barrier();
       for (int c = 0; c < nc; ++c) {
         // chunks 2 .. kPrefetchAhead - 1 at the first iteration, then chunk c + kPrefetchAhead
         const int cbeg = c == 0 ? 2 : c + kPrefetchAhead;
@@ -658,9 +678,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
             pf.ptr[j] += pf.adv[j];
           }
         }
-        __syncthreads();
-        __syncthreads();
-        __syncthreads();
+        dma_barrier();
+        dma_barrier();
+        dma_barrier();
       }
     }
     wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
@@ -670,9 +690,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   if (w >= kOutputWave0) {
     // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  Q H
     // of chunk c is taken between b1 and b2 (H(c) is rewritten in phase 3; the Q tile's slot is
-    // refilled during chunk c + 1), P U~ of chunk c before b1 of chunk c + 1 (U~ alternates between
-    // two buffers), so that nothing of the output path holds b3; the rows are stored between b1 and
-    // b2 of chunk c + 1.
+    // refilled during chunk c + 1), P U~ of chunk c before b1 of chunk c + 1 (U~ is rewritten only
+    // after that barrier), so that nothing of the output path holds b3; the rows are stored between
+    // b1 and b2 of chunk c + 1.
     const int ow = w - kOutputWave0;
     if (nc > 0) {
       unsigned char *ob = reinterpret_cast<unsigned char *>(o + (size_t)h * kDim + d0);
@@ -685,8 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
         if (c > 0) {
-          out_stage(O, pf, decs + ((c - 1) % kDecStages) * kDecBytes, Uo + ((c - 1) & 1) * kXBytes, ow, l,
-                    oslot);
+          out_stage(O, pf, decs + ((c - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
           load_p(pf, rec_at(rec, slot0 + c, h, Hv), ow, l);
         }
         __syncthreads();  // b1
@@ -695,8 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         __syncthreads();  // b2
         __syncthreads();  // b3
       }
-      out_stage(O, pf, decs + ((nc - 1) % kDecStages) * kDecBytes, Uo + ((nc - 1) & 1) * kXBytes, ow, l,
-                oslot);
+      out_stage(O, pf, decs + ((nc - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
       if (write_o) store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
     }
     return;
@@ -726,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       if (pw == 3) wait_vmcnt<kChunkCount(3)>();
       else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
       else wait_vmcnt<kChunkCount(0)>();
-      __syncthreads();
+      dma_barrier();
       for (int c = 0; c < nc; ++c) {
         // Chunk c + 2 is loaded during chunk c, spread over its three phases, into tile and decay
         // slots (c + 2) % 3, which held chunk c - 1 (clamped reloads of the last chunk only go to
@@ -735,9 +753,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         const unsigned tslot = tiles_lds + ((c + 2) % kTileStages) * kTileBytes;
         const uint8_t *tp = rec_at(rec, slot0 + cn, h, Hv);
         dma_tiles<0>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
-        __syncthreads();  // b1
+        dma_barrier();  // b1
         dma_tiles<1>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
-        __syncthreads();  // b2
+        dma_barrier();  // b2
         dma_tiles<2>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
         if (pw == kDecWave) dma_dec(slot0 + cn, h, Hv, l, rec, decs_lds + ((c + 2) % kDecStages) * kDecBytes);
         // Chunk c + 1 (loaded during chunk c - 1) must have landed before b3: loads complete in
@@ -745,7 +763,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         if (pw == 3) wait_vmcnt<kChunkCount(3)>();
         else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
         else wait_vmcnt<kChunkCount(0)>();
-        __syncthreads();  // b3
+        dma_barrier();  // b3
       }
     }
     wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
@@ -772,19 +790,18 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     }
 
   if (nc > 0) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-      store_u32x2(Ht + vmaj(lj, state_key(w, a, 4 * lg)), pack_bf16x2(H[a][0], H[a][1]),
-                  pack_bf16x2(H[a][2], H[a][3]));
+    write_ht(Ht, Htl, H, w, l);
     __syncthreads();
-    // Unrolled over the period of the ring slots and the U~ buffers (3 x 2), so every slot address
-    // is a compile-time offset rather than per-chunk address arithmetic on the compute waves.
+    // Unrolled over twice the period of the ring slots (3), so every slot address is a
+    // compile-time offset rather than per-chunk address arithmetic on the compute waves (a
+    // three-chunk body keeps more values live across its steps and spills).
+    static_assert(kTileStages == 3 && kDecStages == 3, "the unroll assumes 3-slot rings");
     for (int c0 = 0; c0 < nc; c0 += 6) {
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
         if (c0 + u < nc)
-          chunk_step<true>(tiles + (u % kTileStages) * kTileBytes, decs + (u % kDecStages) * kDecBytes, w,
-                           l, H, Ht, Rh, Rl, Uh, Ul, Uo + (u & 1) * kXBytes, ident);
+          chunk_step<true>(tiles + (u % 3) * kTileBytes, decs + (u % 3) * kDecBytes, w, l, H, Ht, Htl, Rh,
+                           Rl, Uh, Ul, Uo, ident);
       }
     }
   }
@@ -818,11 +835,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Htl[kHtBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Rh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Rl[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Uh[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ul[kXBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char Uo[2 * kXBytes];  // chunk c in Uo[c % 2]
+  __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
   __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
 
@@ -843,7 +861,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       Walker pf = cur;  // the step warmed next: steps 2 .. kPrefetchAhead - 1 first
       next_step(pf, gr, cu);
       if (pf.valid) next_step(pf, gr, cu);
-      __syncthreads();
+      dma_barrier();
       PrefetchLane pl;  // lines of chunk 0 of item round pl_k
       int pl_k = -1;
       for (int s = 0; cur.valid; ++s) {
@@ -861,9 +879,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
           }
           next_step(pf, gr, cu);
         }
-        __syncthreads();
-        __syncthreads();
-        __syncthreads();
+        dma_barrier();
+        dma_barrier();
+        dma_barrier();
         next_step(cur, gr, cu);
       }
     }
@@ -889,8 +907,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       __syncthreads();
       for (; cur.valid; ++s) {
         if (s > 0) {
-          out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo + ((s - 1) & 1) * kXBytes, ow, l,
-                    oslot);
+          out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
           load_p(pf, rec_at(rec, cur.it.slot0 + cur.c, cur.it.h, Hv), ow, l);
         }
         __syncthreads();  // b1
@@ -903,8 +920,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         prev = cur;
         next_step(cur, gr, cu);
       }
-      out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo + ((s - 1) & 1) * kXBytes, ow, l,
-                oslot);
+      out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
       store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
                     reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
     }
@@ -940,7 +956,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       if (pw == 3) wait_vmcnt<kChunkCount(3)>();
       else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
       else wait_vmcnt<kChunkCount(0)>();
-      __syncthreads();
+      dma_barrier();
       for (int s = 0; cur.valid; ++s) {
         // Step s + 2 is loaded during step s, spread over its three phases, into tile and decay
         // slots (s + 2) % 3, which held step s - 1 (clamped reloads of the last step only go to
@@ -949,9 +965,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         const unsigned tslot = tiles_lds + ((s + 2) % kTileStages) * kTileBytes;
         const uint8_t *tp = rec_at(rec, ld.it.slot0 + ld.c, ld.it.h, Hv);
         dma_tiles<0>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
-        __syncthreads();  // b1
+        dma_barrier();  // b1
         dma_tiles<1>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
-        __syncthreads();  // b2
+        dma_barrier();  // b2
         dma_tiles<2>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
         if (pw == kDecWave)
           dma_dec(ld.it.slot0 + ld.c, ld.it.h, Hv, l, rec, decs_lds + ((s + 2) % kDecStages) * kDecBytes);
@@ -960,7 +976,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         if (pw == 3) wait_vmcnt<kChunkCount(3)>();
         else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
         else wait_vmcnt<kChunkCount(0)>();
-        __syncthreads();  // b3
+        dma_barrier();  // b3
         next_step(cur, gr, cu);
       }
 #undef GDN_BASES
@@ -971,14 +987,14 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
 
   // Compute waves.  State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].
   // At the last chunk of an item the final state is stored and the next item's initial state,
-  // loaded during that chunk, takes its place before bf16 H goes to LDS.
+  // loaded during that chunk, takes its place before H (hi and lo) goes to LDS.
   Walker cur;
   cur.k = -1;
   next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
   if (!cur.valid) return;
   f32x4 H[2], Hn[2];
   load_h0(H, cur.it, h0, h0_index, num_h0, Hv, d0, w, l);
-  write_ht(Ht, H, w, l);
+  write_ht(Ht, Htl, H, w, l);
   __syncthreads();
   for (int s = 0; cur.valid; ++s) {
     const bool last = cur.c == cur.it.nc - 1;
@@ -988,7 +1004,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
     }
     chunk_step<false>(tiles + (s % kTileStages) * kTileBytes, decs + (s % kDecStages) * kDecBytes, w,
-                      l, H, Ht, Rh, Rl, Uh, Ul, Uo + (s & 1) * kXBytes);
+                      l, H, Ht, Htl, Rh, Rl, Uh, Ul, Uo);
     if (last) {
       store_ht(H, cur.it, hT, Hv, d0, w, l);
       next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
@@ -999,7 +1015,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
     } else {
       ++cur.c;
     }
-    write_ht(Ht, H, w, l);
+    write_ht(Ht, Htl, H, w, l);
     __syncthreads();  // b3
   }
 }

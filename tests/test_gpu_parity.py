@@ -231,3 +231,47 @@ def test_many_tiny_sequences():
         o1, h1 = run_gpu(xs)
         assert np.array_equal(o[sl], o1) and np.array_equal(hT[n], h1[0]), f"sequence {n} differs"
 
+
+
+def test_side_stream_with_binding_allocations():
+    # The binding allocates o, hT and the workspace itself; the call runs on a side stream while
+    # the current stream keeps allocating and writing memory of the same sizes.  The allocations
+    # are recorded on the side stream, so none of that memory may be reused under the call.
+    say("[side-stream] t539_h16x32 on a side stream, allocations on the current stream")
+    x = gi.make_case("t539_h16x32")
+    d = dev_inputs(x)
+    T, N = int(x.cu[-1]), len(x.cu) - 1
+    cu_h = torch.from_numpy(x.cu.astype(np.int64))
+    ws_n = gdn.gdn_chunk_fwd_workspace_size(T, N, 16, 32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], None, stream=side,
+                                      cu_seqlens_host=cu_h))
+        junk = [torch.full((ws_n,), 0xFF, dtype=torch.uint8, device="cuda"),
+                torch.full((T, 32, 128), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                torch.full((N, 32, 128, 128), float("nan"), dtype=torch.float32, device="cuda")]
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    o_ref, h_ref = run_oracle(x)
+    for o, hT in outs:
+        check(o.float().cpu().numpy().astype(np.float64), hT.cpu().numpy().astype(np.float64), o_ref, h_ref,
+              "side stream")
+    assert all(torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) for o, _ in outs)
+
+
+@pytest.mark.parametrize("Hk,Hv", [(8, 16), (1, 4)])
+@pytest.mark.parametrize("decay", ["slow", "none"])
+def test_long_sequence_state_precision(Hk, Hv, decay):
+    # T = 16,384 with a non-symmetric initial state, where the state's rounding error has the most
+    # chunks to build up over: g = log sigmoid(N(6, 1)) (slow decay) or g = 0 (no decay at all).
+    # Hv = 16 runs the plain state pass (one chain of 256 chunk steps); Hv = 4 the time split.
+    say(f"[long-state] T=16384 Hk={Hk} Hv={Hv} decay={decay} h0 std 0.5")
+    x = gi.make_gdn_inputs(Hk, Hv, [16384], seed=400 + Hv, with_h0=True, h0_std=0.5, g_mean=6.0)
+    if decay == "none":
+        x.g[:] = 0.0
+    assert not np.allclose(x.h0[0, 0], x.h0[0, 0].T)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), f"T=16384 Hv={Hv} {decay}")
