@@ -143,17 +143,39 @@ def _check_cu(cu_seqlens, T, cu_host):
     return host.numel() - 1
 
 
-def _stream(stream, device):
-    """The stream to enqueue on: the given one, else the current stream of the tensors' device."""
+def _torch_stream(stream, device):
+    """The stream to enqueue on as a torch stream: the given one (a torch stream or a raw
+    hipStream_t handle), else the current stream of the tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
-def _workspace(workspace, need, device):
-    """A caller's workspace (uint8, contiguous, on the device, at least `need` bytes), or a new one."""
+def _stream(stream, device):
+    return ctypes.c_void_p(_torch_stream(stream, device).cuda_stream)
+
+
+def _keep_for(stream, device, tensors):
+    """Tensors this binding allocated for a call that runs on a stream other than the current
+    one: tell the caching allocator they are in use on that stream, so that once the caller drops
+    them their memory is not handed to a new allocation on the current stream while the call's
+    kernels may still be reading or writing it."""
+    ts = _torch_stream(stream, device)
+    if ts != torch.cuda.current_stream(device):
+        for t in tensors:
+            if t is not None:
+                t.record_stream(ts)
+
+
+def _workspace(workspace, need, device, fresh):
+    """A caller's workspace (uint8, contiguous, on the device, at least `need` bytes), or a new one
+    (appended to `fresh`, the tensors allocated for this call)."""
     if workspace is None:
-        return torch.empty(need, dtype=torch.uint8, device=device)
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        fresh.append(ws)
+        return ws
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != device:
         raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
     if workspace.numel() < need:
@@ -172,18 +194,21 @@ def _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace, cu_seq
     _check(beta, "beta", torch.float32, (T, Hv), dev)
     N = _check_cu(cu_seqlens, T, cu_seqlens_host)
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    fresh = []
     if o is None:
         o = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
+        fresh.append(o)
     _check(o, "o", torch.bfloat16, (T, Hv, D), dev)
     if hT is None and want_state:
         hT = torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+        fresh.append(hT)
     if hT is not None:
         _check(hT, "hT", torch.float32, (N, Hv, D, D), dev)
     need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
     if need == 0:
         raise GdnError(GDN_ERR_SHAPE, "gdn_chunk_fwd_workspace_size")
-    workspace = _workspace(workspace, need, dev)
-    return T, N, Hk, Hv, o, hT, _desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel())
+    workspace = _workspace(workspace, need, dev, fresh)
+    return T, N, Hk, Hv, o, hT, _desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), fresh
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, want_state=True,
@@ -193,14 +218,15 @@ def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, wan
     ``cu_seqlens_host`` (a CPU copy) avoids the device sync of checking ``cu_seqlens``.
     ``workspace`` (uint8 CUDA tensor) may be passed to avoid an allocation per call.
     """
-    T, N, Hk, Hv, o, hT, d = _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace,
-                                       cu_seqlens_host)
+    T, N, Hk, Hv, o, hT, d, fresh = _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace,
+                                              cu_seqlens_host)
     if h0 is not None:
         _check(h0, "h0", torch.float32, (N, Hv, D, D), q.device)
     rc = lib().gdn_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                              _ptr(h0), _ptr(o), _ptr(hT), _stream(stream, q.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd")
+    _keep_for(stream, q.device, fresh)
     return o, hT
 
 
@@ -210,8 +236,8 @@ def gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, *, o=None,
     (h0: fp32 [num_h0, Hv, 128, 128]; h0_index: int32 [N] on the device; an index outside
     [0, num_h0) means a zero state).  One prefix state fans out to many candidates without copies.
     hT may not overlap h0.  Returns (o, hT)."""
-    T, N, Hk, Hv, o, hT, d = _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace,
-                                       cu_seqlens_host)
+    T, N, Hk, Hv, o, hT, d, fresh = _chunk_io(q, k, v, g, beta, cu_seqlens, o, hT, want_state, workspace,
+                                              cu_seqlens_host)
     if h0.dim() != 4 or h0.shape[0] < 1:
         raise ValueError("h0 must be [num_h0, Hv, 128, 128] with num_h0 >= 1")
     _check(h0, "h0", torch.float32, (int(h0.shape[0]), Hv, D, D), q.device)
@@ -221,6 +247,7 @@ def gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, *, o=None,
                                      _ptr(hT), _stream(stream, q.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd_indexed")
+    _keep_for(stream, q.device, fresh)
     return o, hT
 
 
@@ -241,12 +268,19 @@ class ChunkPlan:
         _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
         if h0 is not None:
             _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
-        self.o = o if o is not None else torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
-        self.hT = hT if hT is not None else torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+        self._fresh = []
+        self.o = o
+        if o is None:
+            self.o = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
+            self._fresh.append(self.o)
+        self.hT = hT
+        if hT is None:
+            self.hT = torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+            self._fresh.append(self.hT)
         _check(self.o, "o", torch.bfloat16, (T, Hv, D), dev)
         _check(self.hT, "hT", torch.float32, (N, Hv, D, D), dev)
         need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
-        self.workspace = _workspace(workspace, need, dev)
+        self.workspace = _workspace(workspace, need, dev, self._fresh)
         self.device = dev
         self.desc = _desc(T, N, Hk, Hv, self.workspace.data_ptr(), self.workspace.numel())
         self.args = (q, k, v, g, beta, cu_seqlens, h0)
@@ -257,6 +291,7 @@ class ChunkPlan:
                                   _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_chunk_prep")
+        _keep_for(stream, self.device, self._fresh)
 
     def state_pass(self, stream=None):
         q, k, v, g, beta, cu, h0 = self.args
@@ -264,6 +299,7 @@ class ChunkPlan:
                                   _ptr(self.o), _ptr(self.hT), _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_state_pass")
+        _keep_for(stream, self.device, self._fresh)
 
     def forward(self, stream=None):
         q, k, v, g, beta, cu, h0 = self.args
@@ -271,6 +307,7 @@ class ChunkPlan:
                                  _ptr(h0), _ptr(self.o), _ptr(self.hT), _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_chunk_fwd")
+        _keep_for(stream, self.device, self._fresh)
 
 
 def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16, Hv=32, y=None, hT=None,
@@ -317,21 +354,25 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
         _check(h0, "h0", torch.float32, (S, Hv, D, D), dev)
     if conv_in is not None:
         _check(conv_in, "conv_in", torch.bfloat16, (S, 3, C), dev)
+    fresh = []
     if y is None:
         y = torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev)
+        fresh.append(y)
     _check(y, "y", torch.bfloat16, (T, Hv, D), dev)
     if hT is None and want_state:
         hT = torch.empty((N, Hv, D, D), dtype=torch.float32, device=dev)
+        fresh.append(hT)
     if hT is not None:
         _check(hT, "hT", torch.float32, (N, Hv, D, D), dev)
     if conv_out is None and cont and want_window:
         conv_out = torch.empty((N, 3, C), dtype=torch.bfloat16, device=dev)
+        fresh.append(conv_out)
     if conv_out is not None:
         _check(conv_out, "conv_out", torch.bfloat16, (N, 3, C), dev)
     need = gdn_mixer_fwd_workspace_size(T, N, Hk, Hv, 4, norm_eps)
     if need == 0:
         raise GdnError(GDN_ERR_SHAPE, "gdn_mixer_fwd_workspace_size")
-    workspace = _workspace(workspace, need, dev)
+    workspace = _workspace(workspace, need, dev, fresh)
     m = MixerDesc(_desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), 4, float(norm_eps))
     if cont:
         rc = lib().gdn_mixer_fwd_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
@@ -344,4 +385,5 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
         where = "gdn_mixer_fwd"
     if rc != GDN_OK:
         raise GdnError(rc, where)
+    _keep_for(stream, dev, fresh)
     return y, hT, conv_out

@@ -1,10 +1,10 @@
 // chunk_prep.hip -- state-independent work of every 64-token chunk, all chunks in parallel.
 //
-// The "open-jev-fast" README ("Phase 3", item 1) lists the steps of a chunk: gate cumsum,
-// K K^T, the (I + A)^-1 solve, u and w, the chunk output and the state update; it also notes that
-// the work which does not depend on the recurrent state can run for several chunks side by
-// side while only the state is passed in sequence.  This kernel does all of that state-independent
-// work for every (chunk, v-head) at once; the sequential part lives in state_pass.hip.
+// The fused kernel of the "open-jev-fast" README ("Phase 3", item 1) walks a path's chunks one
+// by one, and for two-chunk paths computes everything that does not involve the recurrent state
+// for both chunks at once.  This kernel takes that split to every chunk: the decay prefix sums,
+// the key Gram products, the triangular inverse and the record derived from them, for every
+// (chunk, v-head) in parallel; the sequential part lives in state_pass.hip.
 //
 // One workgroup per (chunk slot, HP = 1 or 2 v-heads of one k-head), 8 waves per v-head.  Every
 // v-head of a k-head shares K K^T and Q K^T (only the decays and beta tell them apart), so a pair

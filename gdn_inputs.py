@@ -78,6 +78,8 @@ CASES = {
     "t539_h16x32": GdnCase("t539_h16x32", 16, 32, [539], seed=2),
     "varlen7_t677_h0": GdnCase("varlen7_t677_h0", 16, 32, [61, 73, 88, 95, 104, 117, 139], seed=3,
                                with_h0=True),
+    # the mixer layer's shape (T = 936) with the distributions of the rule's own inputs above
+    "t936_h16x32": GdnCase("t936_h16x32", 16, 32, [936], seed=9),
     "t3399_h16x32": GdnCase("t3399_h16x32", 16, 32, [3399], seed=4),
     "t16384_h16x32": GdnCase("t16384_h16x32", 16, 32, [16384], seed=5),
     # one GPU's share of T = 16,384 when the 32 v-heads are split over 8 GPUs by heads

@@ -1,17 +1,18 @@
 /*
  * gdn.h -- libgdn: chunked Gated DeltaNet prefill forward for AMD Instinct MI355X (gfx950).
  *
- * The operation is the gated delta rule, the recurrent linear-attention computation of the
- * Gated DeltaNet layers (System1-Omni PR #186 page, "Purpose and summary"; computed in 64-token
- * chunks as the "open-jev-fast" README describes under "Phase 3", item 1, after the Gated
- * DeltaNet paper it cites as reference [5]):
+ * The operation is the gated delta rule, the recurrence inside the model's linear-attention
+ * (Gated DeltaNet) layers (System1-Omni PR #186 page, "Purpose and summary"), evaluated 64
+ * tokens at a time as in the fused kernel of the "open-jev-fast" README ("Phase 3", item 1),
+ * which follows the Gated DeltaNet paper it lists as reference [5]:
  *
  *     S_t = exp(g_t) * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *     o_t = S_t q_t
  *
  * over packed variable-length sequences, each with its own optional fp32 initial state (the
- * prefix-continuation form: the "open-jev-fast" README, "Phase 2" item 2, hands a prefix's final
- * recurrent state to each candidate; PR #186, "Review scope and map", keeps per-candidate state).
+ * prefix-continuation form: in the "open-jev-fast" README, "Phase 2" item 2, a long prompt's
+ * end state seeds every candidate that continues it; PR #186, "Review scope and map", keeps a
+ * separate state per candidate).
  * There is no 1/sqrt(dk) scale on q: o_t = S_t q_t exactly.
  *
  * Conventions shared by every entry point
@@ -82,18 +83,27 @@ typedef struct {
   size_t workspace_bytes;
 } gdn_chunk_desc;
 
-/* ABI version of the loaded library (GDN_ABI_VERSION at build time). */
+/* ABI version of the loaded library (GDN_ABI_VERSION at build time).  The PR #186 page keeps its
+ * device library behind a numbered binary interface ("Purpose and summary": version 9 there) and
+ * runs a contract check of it ("Test plan and results"); a caller compares this number with the
+ * header it was built against.  Never fails. */
 GDN_EXPORT int gdn_abi_version(void);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL; unknown codes get a generic
+ * text).  Part of the error paths of the library interface that the PR #186 page's review covers
+ * ("Review scope and map": callers, error and resource paths inspected). */
 GDN_EXPORT const char *gdn_status_string(int status);
 
-/* hipError_t of the calling thread's last GDN_ERR_HIP, 0 if none. */
+/* hipError_t of the calling thread's last GDN_ERR_HIP, 0 if none (thread-local; never fails).
+ * The HIP side of the same error paths (PR #186 page, "Review scope and map"). */
 GDN_EXPORT int gdn_last_hip_error(void);
 
 /* Workspace bytes gdn_chunk_fwd needs for this shape; 0 if the description is invalid.
  * The workspace and pointer fields of *d are ignored.  One sequence (N = 1) of at least 32 chunks
- * with at most 8 v-heads needs 6 MiB more: its state pass may run split along time (below). */
+ * with at most 8 v-heads needs 6 MiB more: its state pass may run split along time (below).
+ * The caller owns the scratch and its lifetime, as the PR #186 page's library does ("Review
+ * scope and map": workspace checked against the plan, scratch address lifetime owned by the
+ * executor, dirty-workspace tests). */
 GDN_EXPORT size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d);
 
 /*
@@ -102,9 +112,10 @@ GDN_EXPORT size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d);
  *   h0 : initial states, or NULL for zero states (device)
  *   o  : output (device), written for every token
  *   hT : final states, or NULL to skip them (device); may equal h0
- * Computes in 64-token chunks: per chunk a local cumsum of g, the K K^T / (I + A)^-1 UT
- * transform, a sequential inter-chunk state pass with fp32 state, and the chunk output
- * ("open-jev-fast" README, "Phase 3" item 1, names these steps).  A single sequence whose heads
+ * Works in 64-token chunks: in each chunk the prefix sums of g, the key Gram matrix and the
+ * unit-lower-triangular inverse of the UT transform, then a pass over the chunks in order that
+ * carries the fp32 state and emits the outputs (the step list of the "open-jev-fast" README's
+ * fused kernel, "Phase 3" item 1).  A single sequence whose heads
  * would leave most of the device idle has its state pass split along time (segment end states,
  * segment transitions, a scan of the segment states, then the outputs); the results meet the same
  * tolerances, and are not bitwise those of a call on a different batch shape.
@@ -114,9 +125,9 @@ GDN_EXPORT int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void 
                   void *o, float *hT, void *stream);
 
 /*
- * gdn_chunk_fwd with the initial states drawn from a pool by index: one prefix's final state
- * handed to each of several candidates without copying it ("open-jev-fast" README, "Phase 2"
- * item 2; PR #186, "Review scope and map", per-candidate state).
+ * gdn_chunk_fwd with the initial states drawn from a pool by index: one prefix's end state seeds
+ * several candidates without being copied ("open-jev-fast" README, "Phase 2" item 2; PR #186,
+ * "Review scope and map", a separate state per candidate).
  *   h0       : fp32 [num_h0, Hv, dk, dv] (device), num_h0 >= 1
  *   h0_index : int32 [N] (device).  Sequence n starts from h0[h0_index[n]]; an index outside
  *              [0, num_h0) means a zero state (the library cannot check device values, so an
@@ -133,9 +144,9 @@ GDN_EXPORT int gdn_chunk_fwd_indexed(const gdn_chunk_desc *d, const void *q, con
 
 /*
  * The two stages of gdn_chunk_fwd, callable on their own (gdn_chunk_fwd = gdn_chunk_prep, then
- * gdn_state_pass, on one stream with one workspace).  The "open-jev-fast" README ("Phase 3",
- * item 1) separates the work that does not depend on the recurrent state, which runs for many
- * chunks side by side, from the state that is passed chunk to chunk.
+ * gdn_state_pass, on one stream with one workspace).  The split generalises the two-chunk path
+ * of the "open-jev-fast" README ("Phase 3", item 1), which computes what does not involve the
+ * recurrent state for both chunks at once and carries only the state from one to the next.
  *
  * gdn_chunk_prep: for every (chunk, v-head) in parallel -- local cumsum of g, K K^T and Q K^T,
  *   A = beta_i e^{G_i - G_j} k_i.k_j (i > j), T = (I + A)^-1 -- writes one record per (chunk,
@@ -154,8 +165,9 @@ GDN_EXPORT int gdn_state_pass(const gdn_chunk_desc *d, const void *q, const void
                               float *hT, void *stream);
 
 /*
- * GDN mixer: the gated delta rule with its input prep and output norm ("open-jev-fast" README,
- * "Phase 2" item 1: causal conv, SiLU, q/k/v split, L2 norm; gated RMSNorm).
+ * GDN mixer: the gated delta rule between its input prep -- a depthwise causal convolution with
+ * SiLU, the split into q, k and v, and the L2 normalisation of q and k -- and its SiLU-gated
+ * RMSNorm (the "open-jev-fast" README, "Phase 2" item 1, has one fused kernel for each side).
  *   qkv    : bf16 [T, 2*Hk*dk + Hv*dv], channels q | k | v, head-major inside each block
  *   conv_w : bf16 [2*Hk*dk + Hv*dv, conv_taps]; tap conv_taps-1 multiplies the current token;
  *            the window holds zeros before every sequence start (no bias)
@@ -180,9 +192,9 @@ GDN_EXPORT int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const voi
 
 /*
  * The mixer continuing from carried states: beside the recurrent state, each sequence carries
- * the conv input window -- the last conv_taps - 1 rows of qkv before it -- so that a prefix's
- * window and state can be handed on to the candidates that continue it ("open-jev-fast" README,
- * "Phase 2" item 2).  C = 2*Hk*dk + Hv*dv, W = conv_taps - 1 (= 3).
+ * the conv input window -- the last conv_taps - 1 rows of qkv before it -- so that both can pass
+ * from a prefix to the candidates that continue it (the "open-jev-fast" README, "Phase 2" item 2,
+ * keeps the window and the recurrent state of a candidate's path identical to a full run).  C = 2*Hk*dk + Hv*dv, W = conv_taps - 1 (= 3).
  *   h0       : fp32 [num_states, Hv, dk, dv] or NULL (zero states)
  *   conv_in  : bf16 [num_states, W, C] or NULL (zeros before every sequence), oldest row first:
  *              row W-1 is the input just before the sequence's first token
