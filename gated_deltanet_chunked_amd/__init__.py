@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
     gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
     gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, ...) -> (o, hT)
     gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, ...) -> (o, hT)
+    gdn_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, h0, o=..., hT=...): gdn_chunk_fwd on the
+        library's static scratch, for callers that cannot allocate (outputs passed in)
     gdn_chunk_prep / gdn_state_pass: the two stages of gdn_chunk_fwd (see ChunkPlan)
     gdn_mixer_fwd_workspace_size(T, N, Hk, Hv)
     gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, ...) -> (y, hT)
@@ -33,9 +35,12 @@ D = 128
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED = 0, 1, 2, 3
 GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_ALIAS, GDN_ERR_HIP = 4, 5, 6, 7
+GDN_ERR_SCRATCH_LIMIT = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_last_hip_error",
-                    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_indexed", "gdn_chunk_prep",
+                    "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_indexed",
+                    "gdn_chunk_fwd_noalloc", "gdn_chunk_prep",
                     "gdn_state_pass", "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd", "gdn_mixer_fwd_cont")
 
 
@@ -78,6 +83,8 @@ def lib():
         L.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc)]
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 10
+        L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+        L.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 10
         L.gdn_chunk_fwd_indexed.restype = ctypes.c_int
         L.gdn_chunk_fwd_indexed.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 7 + [ctypes.c_int32] + [P] * 4
         L.gdn_chunk_prep.restype = ctypes.c_int
@@ -248,6 +255,36 @@ def gdn_chunk_fwd_indexed(q, k, v, g, beta, cu_seqlens, h0, h0_index, *, o=None,
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd_indexed")
     _keep_for(stream, q.device, fresh)
+    return o, hT
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, h0=None, *, o, hT=None, stream=None,
+                          cu_seqlens_host=None):
+    """gdn_chunk_fwd on the library's static device scratch instead of a workspace, for callers
+    that cannot allocate: the outputs o (bf16 [T, Hv, 128]) and, if wanted, hT (fp32
+    [N, Hv, 128, 128]) are passed in, and nothing is allocated here or in the library.  Shapes
+    whose workspace would exceed NOALLOC_SCRATCH_BYTES raise GdnError(GDN_ERR_SCRATCH_LIMIT).
+    Calls that overlap in time on one GPU share the scratch and race; order them on one stream.
+    Returns (o, hT)."""
+    dev = q.device
+    T, Hk, Hv = int(q.shape[0]), int(q.shape[1]), int(v.shape[1])
+    _check(q, "q", torch.bfloat16, (T, Hk, D), dev)
+    _check(k, "k", torch.bfloat16, (T, Hk, D), dev)
+    _check(v, "v", torch.bfloat16, (T, Hv, D), dev)
+    _check(g, "g", torch.float32, (T, Hv), dev)
+    _check(beta, "beta", torch.float32, (T, Hv), dev)
+    N = _check_cu(cu_seqlens, T, cu_seqlens_host)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    _check(o, "o", torch.bfloat16, (T, Hv, D), dev)
+    if hT is not None:
+        _check(hT, "hT", torch.float32, (N, Hv, D, D), dev)
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (N, Hv, D, D), dev)
+    d = _desc(T, N, Hk, Hv)
+    rc = lib().gdn_chunk_fwd_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(hT), _stream(stream, dev))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_noalloc")
     return o, hT
 
 

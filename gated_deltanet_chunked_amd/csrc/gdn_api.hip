@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gdn.h"
 #include "gdn_device.h"
@@ -246,6 +247,48 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------------
+// Scratch of gdn_chunk_fwd_noalloc: the chunk path's workspace (records, time-split states) for
+// callers that cannot allocate.  Every GPU that loads the library holds its own copy of this
+// array until the process ends.  In host code `scratch` names a host-side stand-in, not a device
+// address: only the per-device address from hipGetSymbolAddress ever reaches a kernel.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the stream's device's copy of `scratch`, looked up once per device with
+// that device current (the caller's current device is restored).  A failed lookup is kept and
+// reported on every later call for that device.
+int scratch_address(hipStream_t stream, void **out) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return record_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    hipError_t err = hipGetDevice(&cur);
+    if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+    void *p = nullptr;
+    if (err == hipSuccess) err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    g_scratch_ptr[dev] = err == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = err;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return record_hip(g_scratch_err[dev]);
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
@@ -260,6 +303,8 @@ const char *gdn_status_string(int status) {
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps an input or the workspace";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP launch failed (see gdn_last_hip_error)";
+    case GDN_ERR_SCRATCH_LIMIT:
+      return "GDN_ERR_SCRATCH_LIMIT: the shape needs more than the static scratch of gdn_chunk_fwd_noalloc";
     default: return "unknown gdn status";
   }
 }
@@ -281,6 +326,26 @@ int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const v
   if (st != GDN_OK) return st;
   return run_chunk(s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT, d->workspace,
                    static_cast<hipStream_t>(stream));
+}
+
+int gdn_chunk_fwd_noalloc(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, const int32_t *cu_seqlens,
+                          const float *h0, void *o, float *hT, void *stream) {
+  Shape s;
+  int st = check_shape(d, s);
+  if (st != GDN_OK) return st;
+  if (s.ws_bytes > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH_LIMIT;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  st = scratch_address(strm, &ws);
+  if (st != GDN_OK) return st;
+  gdn_chunk_desc dd = *d;
+  dd.workspace = ws;
+  dd.workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+  StatePool pool{h0, 0, nullptr};
+  st = check_chunk_args(&dd, s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT);
+  if (st != GDN_OK) return st;
+  return run_chunk(s, kBoth, q, k, v, g, beta, cu_seqlens, pool, o, hT, ws, strm);
 }
 
 int gdn_chunk_fwd_indexed(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,

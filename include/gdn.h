@@ -68,8 +68,13 @@ typedef enum {
   GDN_ERR_ALIGN = 4,       /* a pointer is not aligned as required                          */
   GDN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the required size              */
   GDN_ERR_ALIAS = 6,       /* an output overlaps an input or the workspace (hT == h0 is ok) */
-  GDN_ERR_HIP = 7          /* a HIP launch failed; see gdn_last_hip_error()                 */
+  GDN_ERR_HIP = 7,         /* a HIP launch failed; see gdn_last_hip_error()                 */
+  GDN_ERR_SCRATCH_LIMIT = 8 /* gdn_chunk_fwd_noalloc: the shape needs more scratch than the
+                               library's static buffer (GDN_NOALLOC_SCRATCH_BYTES)            */
 } gdn_status;
+
+/* Size of the static device scratch behind gdn_chunk_fwd_noalloc (per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Problem description.  Sizes are host values; nothing is read from device memory. */
 typedef struct {
@@ -123,6 +128,29 @@ GDN_EXPORT size_t gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *d);
 GDN_EXPORT int gdn_chunk_fwd(const gdn_chunk_desc *d, const void *q, const void *k, const void *v,
                   const float *g, const float *beta, const int32_t *cu_seqlens, const float *h0,
                   void *o, float *hT, void *stream);
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc.  Arguments and results are gdn_chunk_fwd's,
+ * but d->workspace and d->workspace_bytes are ignored: the records and state buffers live in the
+ * library's own scratch, a static device array of GDN_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU
+ * the library runs on, held until the process ends.
+ *  * Limit: gdn_chunk_fwd_workspace_size(d) <= GDN_NOALLOC_SCRATCH_BYTES, else
+ *    GDN_ERR_SCRATCH_LIMIT with nothing launched (at Hv = 32: T / 64 + N <= 110, e.g. one sequence
+ *    of up to 7,039 tokens).  Every other check and error is gdn_chunk_fwd's.
+ *  * Allocates nothing and frees nothing.  The first call on a GPU looks up that GPU's copy of the
+ *    array (hipGetSymbolAddress, with the GPU made current for the lookup and the previous
+ *    current device restored); make one call before capturing a graph.  A failed lookup is
+ *    GDN_ERR_HIP, on that call and every later one on that GPU.
+ *  * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ *    different streams, or from host threads without ordering) race and give wrong results.
+ *    Calls ordered on one stream are safe.  The array keeps the last call's contents; nothing in
+ *    it needs clearing, since each call writes every byte of it that the call reads.
+ */
+GDN_EXPORT int gdn_chunk_fwd_noalloc(const gdn_chunk_desc *d, const void *q, const void *k,
+                                     const void *v, const float *g, const float *beta,
+                                     const int32_t *cu_seqlens, const float *h0, void *o, float *hT,
+                                     void *stream);
 
 /*
  * gdn_chunk_fwd with the initial states drawn from a pool by index: one prefix's end state seeds

@@ -39,7 +39,7 @@ def test_abi_version_and_status_strings():
     m = re.search(r"#define GDN_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == gdn.gdn_abi_version()
     names = ["GDN_OK", "GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_UNSUPPORTED", "GDN_ERR_ALIGN",
-             "GDN_ERR_WORKSPACE", "GDN_ERR_ALIAS", "GDN_ERR_HIP"]
+             "GDN_ERR_WORKSPACE", "GDN_ERR_ALIAS", "GDN_ERR_HIP", "GDN_ERR_SCRATCH_LIMIT"]
     for code, name in enumerate(names):
         assert gdn.gdn_status_string(code).startswith(name)
     assert "unknown" in gdn.gdn_status_string(99)
@@ -240,3 +240,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib_handle", None)
     with pytest.raises(RuntimeError, match="missing"):
         gdn.gdn_abi_version()
+
+
+def test_noalloc_scratch_limit():
+    # The scratch limit is checked on the host before the static scratch is looked up or anything
+    # is launched: a shape whose workspace exceeds it is rejected, an invalid shape keeps its own
+    # status, and the limit in the header matches the binding's.
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == gdn.NOALLOC_SCRATCH_BYTES
+    L = gdn.lib()
+    a = _addrs()
+    args = [ctypes.c_void_p(a[n]) for n in ("q", "k", "v", "g", "beta", "cu", "h0", "o", "hT")] + [None]
+    for (T_, N_, Hk_, Hv_) in [(7040, 1, 16, 32), (16384, 1, 16, 32), (64 * 1000, 1, 1, 4)]:
+        assert gdn.gdn_chunk_fwd_workspace_size(T_, N_, Hk_, Hv_) > gdn.NOALLOC_SCRATCH_BYTES
+        d = gdn.ChunkDesc(T_, N_, Hk_, Hv_, 128, 128, None, 0)
+        rc = L.gdn_chunk_fwd_noalloc(ctypes.byref(d), *args)
+        assert rc == gdn.GDN_ERR_SCRATCH_LIMIT, (T_, rc)
+    assert gdn.gdn_chunk_fwd_workspace_size(7039, 1, 16, 32) <= gdn.NOALLOC_SCRATCH_BYTES
+    d = gdn.ChunkDesc(10, 1, 3, 4, 128, 128, None, 0)  # Hv % Hk != 0
+    assert L.gdn_chunk_fwd_noalloc(ctypes.byref(d), *args) == gdn.GDN_ERR_SHAPE
+    assert L.gdn_chunk_fwd_noalloc(None, *args) == gdn.GDN_ERR_NULL
