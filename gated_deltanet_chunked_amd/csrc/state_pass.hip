@@ -26,7 +26,8 @@
 //            hi/lo and plain) to LDS
 //            output waves:  the previous chunk's rows to memory; Q H                 -> b2
 //   phase 3: compute waves: H update, H (bf16 hi and lo) to LDS                      -> b3
-// so the output path of chunk c finishes during chunk c + 1, off the chunk's last barrier.
+// so the output path of chunk c finishes during chunk c + 1, off the chunk's last barrier (the
+// persistent kernel runs it between b2 and b3 of chunk c instead; see there).
 // Thirteen waves per workgroup:
 //   * 4 compute waves (one per SIMD) keep the state and do no global access in the chunk loop.
 //   * 4 producer waves issue the bulk loads as global->LDS loads (global_load_lds_dwordx4: 1 KiB
@@ -332,8 +333,8 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
 // its own global->LDS loads still in flight, which would tie these reads to load latency.  out_qh
 // runs between b1 and b2: Q H needs the chunk's entry state, which the compute waves overwrite in
 // phase 3, and the Q tile's slot is not refilled before chunk c + 1.  out_stage runs once U~ is in
-// LDS, after the chunk's last barrier and before b1 of the next chunk (the compute waves rewrite
-// U~ only after that b1, so one buffer serves): it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg .. + 3
+// LDS (after b2; the compute waves rewrite U~ only after b1 of the next chunk, so one buffer
+// serves): it adds P U~ and stages the rows in this wave's LDS slot (lane-linear: rows 4 lg .. + 3
 // of column lj at byte 8 l); they are read back transposed and stored between b1 and b2 of the
 // next chunk (store_o).
 __device__ __forceinline__ f32x4 out_qh(const unsigned char *qt, const unsigned char *Ht, int w, int l) {
@@ -890,9 +891,11 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   }
 
   if (w >= kOutputWave0) {
-    // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  As in
-    // the single-round kernel: Q H of step s between b1 and b2, P U~ of step s before b1 of step
-    // s + 1, the rows stored between b1 and b2 of step s + 1.
+    // Output waves: o = e^G o (Q H) + P U~ for row block ow.  Barriers as the compute waves.  Q H
+    // of step s between b1 and b2, then P U~, the rows' store and the next step's P load between b2
+    // and b3 (U~ of step s is in LDS from b2 on and is rewritten only after b1 of step s + 1).
+    // Unlike in the single-round kernel, whose b3 they would hold up, that is faster here (7
+    // sequences at T = 677: 33.0 -> 31.0 us per pass, interleaved on one box).
     const int ow = w - kOutputWave0;
     Walker cur = first_step(gr, cu);
     if (cur.valid) {
@@ -901,28 +904,19 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
                             8 * ((l & 15) >> 2);
       PFrags pf;
       load_p(pf, rec_at(rec, cur.it.slot0, cur.it.h, Hv), ow, l);
-      Walker prev = cur;
-      f32x4 O = zero4();
-      int s = 0;
       __syncthreads();
-      for (; cur.valid; ++s) {
-        if (s > 0) {
-          out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
-          load_p(pf, rec_at(rec, cur.it.slot0 + cur.c, cur.it.h, Hv), ow, l);
-        }
+      for (int s = 0; cur.valid; ++s) {
         __syncthreads();  // b1
-        if (s > 0)
-          store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
-                        reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
-        O = out_qh(tiles + (s % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
+        const f32x4 O = out_qh(tiles + (s % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
-        __syncthreads();  // b3
-        prev = cur;
+        out_stage(O, pf, decs + (s % kDecStages) * kDecBytes, Uo, ow, l, oslot);
+        const int c_ = cur.c, tb_ = cur.it.tb, te_ = cur.it.te, h_ = cur.it.h;
         next_step(cur, gr, cu);
+        if (cur.valid) load_p(pf, rec_at(rec, cur.it.slot0 + cur.c, cur.it.h, Hv), ow, l);
+        store_o<kONt>(c_, tb_, te_, Hv, ow, l, oslot, reinterpret_cast<unsigned char *>(o + (size_t)h_ * kDim + d0),
+                      ooff);
+        __syncthreads();  // b3
       }
-      out_stage(O, pf, decs + ((s - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
-      store_o<kONt>(prev.c, prev.it.tb, prev.it.te, Hv, ow, l, oslot,
-                    reinterpret_cast<unsigned char *>(o + (size_t)prev.it.h * kDim + d0), ooff);
     }
     return;
   }
