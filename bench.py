@@ -31,6 +31,7 @@ Workloads (seeded, synthetic; see gdn_inputs.py):
     t256_h4, t539_h16x32, varlen7_t677_h0, t936_h16x32, t3399_h16x32
     t16384_h2x4      T=16384 at Hk=2, Hv=4: one GPU's share when the heads are split over 8 GPUs
     mixer_t936_x48   48 GDN mixer layers at T=936, Hk=16, Hv=32, one layer per seed
+                     (--fused-norm: gdn_mixer_fwd_fused_norm, the norm inside the state pass)
 """
 from __future__ import annotations
 
@@ -229,6 +230,8 @@ def main():
     ap.add_argument("--rotate-mib", type=float, default=512.0,
                     help="rotate among input copies until their footprint exceeds this (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-norm", action="store_true",
+                    help="mixer workload: gated RMSNorm fused into the state pass (gdn_mixer_fwd_fused_norm)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on oracle time for the baseline")
     ap.add_argument("--copy-mib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration under rocprofv3)")
@@ -304,7 +307,8 @@ def main():
         def step(i):
             for l, L_ in enumerate(layers):
                 gdn.gdn_mixer_fwd(L_["qkv"], L_["conv_w"], L_["g"], L_["beta"], L_["z"], L_["norm_w"], L_["cu"],
-                                  None, y=ys[l], hT=hs[l], workspace=ws, cu_seqlens_host=cu_host)
+                                  None, y=ys[l], hT=hs[l], workspace=ws, cu_seqlens_host=cu_host,
+                                  fused_norm=args.fused_norm)
         tokens_per_step = T * LAYERS
         layers_per_step = LAYERS
 
@@ -423,6 +427,8 @@ def main():
 
     cfg = {"workload": args.workload, "T": T, "N": N, "Hk": Hk, "Hv": Hv, "d": D, "chunk": 64,
            "rotating_input_sets": R, "layers_per_step": layers_per_step}
+    if mixer:
+        cfg["norm"] = "fused into the state pass" if args.fused_norm else "separate kernel"
     line = {"metric": "GDN prefill tokens/s per layer (Hk16/Hv32,d128) + % MFMA/HBM roofline",
             "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,

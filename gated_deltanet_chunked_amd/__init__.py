@@ -41,7 +41,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_last_hip_error",
                     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_indexed",
                     "gdn_chunk_fwd_noalloc", "gdn_chunk_prep",
-                    "gdn_state_pass", "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd", "gdn_mixer_fwd_cont")
+                    "gdn_state_pass", "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd", "gdn_mixer_fwd_cont",
+                    "gdn_mixer_fwd_fused_norm")
 
 
 class ChunkDesc(ctypes.Structure):
@@ -95,6 +96,8 @@ def lib():
         L.gdn_mixer_fwd_workspace_size.argtypes = [ctypes.POINTER(MixerDesc)]
         L.gdn_mixer_fwd.restype = ctypes.c_int
         L.gdn_mixer_fwd.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11
+        L.gdn_mixer_fwd_fused_norm.restype = ctypes.c_int
+        L.gdn_mixer_fwd_fused_norm.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11
         L.gdn_mixer_fwd_cont.restype = ctypes.c_int
         L.gdn_mixer_fwd_cont.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 9 + [ctypes.c_int32] + [P] * 5
         _lib_handle = L
@@ -348,10 +351,13 @@ class ChunkPlan:
 
 
 def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16, Hv=32, y=None, hT=None,
-                  want_state=True, norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
-    """GDN mixer forward (conv + SiLU + L2 norm, the chunked rule, gated RMSNorm).  Returns (y, hT)."""
+                  want_state=True, norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None,
+                  fused_norm=False):
+    """GDN mixer forward (conv + SiLU + L2 norm, the chunked rule, gated RMSNorm).  Returns (y, hT).
+    fused_norm=True calls gdn_mixer_fwd_fused_norm (the norm inside the state pass; slower on
+    MI355X, and GdnError(GDN_ERR_UNSUPPORTED) where the work items do not fit in one round)."""
     y, hT, _ = _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, None, None, False, Hk, Hv, y, hT, None,
-                      want_state, False, norm_eps, workspace, stream, cu_seqlens_host)
+                      want_state, False, norm_eps, workspace, stream, cu_seqlens_host, fused_norm)
     return y, hT
 
 
@@ -368,7 +374,7 @@ def gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, con
 
 
 def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, cont, Hk, Hv, y, hT, conv_out,
-           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host):
+           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host, fused_norm=False):
     dev = qkv.device
     T = int(qkv.shape[0])
     C = (2 * Hk + Hv) * D
@@ -417,9 +423,10 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
                                       _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream, dev))
         where = "gdn_mixer_fwd_cont"
     else:
-        rc = lib().gdn_mixer_fwd(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
-                                 _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream, dev))
-        where = "gdn_mixer_fwd"
+        fn, where = ((lib().gdn_mixer_fwd_fused_norm, "gdn_mixer_fwd_fused_norm") if fused_norm
+                     else (lib().gdn_mixer_fwd, "gdn_mixer_fwd"))
+        rc = fn(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
+                _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream, dev))
     if rc != GDN_OK:
         raise GdnError(rc, where)
     _keep_for(stream, dev, fresh)

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec,
-    ConvArgs ca) {
+    ConvArgs ca, uint32_t *__restrict__ norm_part) {
   static_assert(!kConv || HP == 2, "the input prep runs on pairs of v-heads");
   constexpr int kThreads = 64 * kWavesPerHead * HP, kWaves = kWavesPerHead * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kConv ? kLdsBytes : kOffW];
@@ -171,6 +171,13 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
   if (t0 >= te) return;  // slot unused (uniform across the workgroup)
   const int L = min(kChunk, te - t0);
   uint8_t *const rec_slot = rec + (size_t)slot * Hv * kRecBytes;  // v-head x at + x * kRecBytes
+  // With the gated RMSNorm fused into the state pass: mark this chunk's row sums of squares of
+  // the group's v-heads as not yet written (one word per thread: 64 rows x HP heads x 8 tiles).
+  if (norm_part) {
+    const int r = tid / (HP * kDvTiles), x = (tid / kDvTiles) % HP, tile = tid % kDvTiles;
+    if (r < L) norm_part[((size_t)(t0 + r) * Hv + h_first + x) * kDvTiles + tile] = kPartEmpty;
+  }
+  static_assert(kThreads == kChunk * HP * kDvTiles, "one word of norm_part per thread");
 
   // ---- 1. global loads up front; gate cumsum per v-head --------------------------------------
   constexpr int kIt = 1024 / kThreads;  // 16-byte pieces of one 64 x 128 tile per thread
@@ -513,18 +520,18 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
 
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, hipStream_t stream) {
+                       void *rec, uint32_t *norm_part, hipStream_t stream) {
   const unsigned short *qp = static_cast<const unsigned short *>(q);
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
   if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
     hipLaunchKernelGGL((chunk_prep_kernel<2, false>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
                        dim3(128 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
-                       ConvArgs{});
+                       ConvArgs{}, norm_part);
   else
     hipLaunchKernelGGL((chunk_prep_kernel<1, false>), dim3((unsigned)nslots, (unsigned)Hv),
                        dim3(64 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
-                       ConvArgs{});
+                       ConvArgs{}, norm_part);
 }
 
 // The same with q, k, v made from the packed mixer input (Hv / Hk even): writes q, k, v (q/k
@@ -533,7 +540,7 @@ void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *con
                             const int32_t *state_index, int num_states, const float *g,
                             const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
                             int64_t nslots, void *rec, void *qo, void *ko, void *vo,
-                            hipStream_t stream) {
+                            uint32_t *norm_part, hipStream_t stream) {
   const ConvArgs ca{static_cast<const unsigned short *>(qkv), static_cast<const unsigned short *>(conv_w),
                     static_cast<const unsigned short *>(conv_in), state_index, num_states,
                     static_cast<unsigned short *>(qo), static_cast<unsigned short *>(ko),
@@ -541,7 +548,7 @@ void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *con
   hipLaunchKernelGGL((chunk_prep_kernel<2, true>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
                      dim3(128 * kWavesPerHead), 0, stream, (const unsigned short *)nullptr,
                      (const unsigned short *)nullptr, g, beta, cu, (int)T, N, Hk, Hv,
-                     static_cast<uint8_t *>(rec), ca);
+                     static_cast<uint8_t *>(rec), ca, norm_part);
 }
 
 }  // namespace gdn

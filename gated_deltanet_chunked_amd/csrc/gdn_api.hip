@@ -13,18 +13,18 @@
 namespace gdn {
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
                        const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, hipStream_t stream);
-void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
-                       const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
-                       const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
-                       hipStream_t stream, SplitPass sp);
+                       void *rec, uint32_t *norm_part, hipStream_t stream);
+hipError_t launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
+                             const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
+                             const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
+                             hipStream_t stream, SplitPass sp, const NormOut *norm);
 void launch_state_scan(const float *phi, const float *bend, const float *h0, const int32_t *h0_index,
                        int num_h0, float *hs, int segs, int Hv, hipStream_t stream);
 void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
                             const int32_t *state_index, int num_states, const float *g,
                             const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
                             int64_t nslots, void *rec, void *qo, void *ko, void *vo,
-                            hipStream_t stream);
+                            uint32_t *norm_part, hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, const void *conv_in, const int32_t *state_index,
                        int num_states, void *q, void *k, void *v, hipStream_t stream);
@@ -203,14 +203,17 @@ gdn::SplitPass plan_split(const Shape &s, int max_groups) {
   return sp;
 }
 
-// Enqueues the checked stages.
+// Enqueues the checked stages.  With norm (the mixer's fused gated RMSNorm, planned by the caller
+// only where fused_norm_ok holds) the pass writes y instead of o, and the prep marks the row sums
+// of squares as not yet written.
 int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const void *v,
               const float *g, const float *beta, const int32_t *cu, const StatePool &pool, void *o,
-              float *hT, void *ws, hipStream_t stream) {
+              float *hT, void *ws, hipStream_t stream, const gdn::NormOut *norm = nullptr) {
   unsigned char *rec = static_cast<unsigned char *>(ws);
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   if ((stage & kPrep) && s.T > 0) {
-    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec, stream);
+    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec,
+                           norm ? norm->part : nullptr, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
   }
@@ -222,25 +225,28 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
       float *bend = reinterpret_cast<float *>(rec + s.rec_bytes);
       float *phi = bend + (size_t)gdn::kSplitStates * gdn::kDim * gdn::kDim;
       float *hs = phi + (size_t)gdn::kSplitStates * gdn::kDim * gdn::kDim;
+      if (norm) return GDN_ERR_UNSUPPORTED;  // never planned (fused_norm_ok)
       sp.mode = 0;
       sp.h_out = bend;
-      gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk, s.Hv,
-                             groups, stream, sp);
+      hipError_t e = gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk,
+                                            s.Hv, groups, stream, sp, nullptr);
+      if (e != hipSuccess) return record_hip(e);
       sp.mode = 1;
       sp.h_out = phi;
-      gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk, s.Hv,
-                             groups, stream, sp);
+      e = gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk, s.Hv,
+                                 groups, stream, sp, nullptr);
+      if (e != hipSuccess) return record_hip(e);
       gdn::launch_state_scan(phi, bend, pool.h0, pool.index, pool.rows, hs, sp.segs, s.Hv, stream);
+      e = hipGetLastError();
+      if (e != hipSuccess) return record_hip(e);
       sp.mode = 2;
       sp.h_in = hs;
       sp.h_out = nullptr;
-      gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, hT, rec, s.T, s.N, s.Hk, s.Hv, groups,
-                             stream, sp);
-    } else {
-      gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T, s.N, s.Hk,
-                             s.Hv, groups, stream, sp);
+      return record_hip(gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, hT, rec, s.T, s.N, s.Hk,
+                                               s.Hv, groups, stream, sp, nullptr));
     }
-    return record_hip(hipGetLastError());
+    return record_hip(gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T,
+                                             s.N, s.Hk, s.Hv, groups, stream, sp, norm));
   }
   return GDN_OK;
 }
@@ -393,7 +399,7 @@ int gdn_state_pass(const gdn_chunk_desc *d, const void *q, const void *k, const 
 namespace {
 struct MixerLayout {
   Shape s;
-  size_t chunk_bytes, q_bytes, v_bytes, total;
+  size_t chunk_bytes, q_bytes, v_bytes, part_bytes, total;
 };
 int mixer_layout(const gdn_mixer_desc *d, MixerLayout &m) {
   if (!d) return GDN_ERR_NULL;
@@ -406,8 +412,28 @@ int mixer_layout(const gdn_mixer_desc *d, MixerLayout &m) {
   m.chunk_bytes = m.s.ws_bytes;
   m.q_bytes = round_up((size_t)m.s.T * m.s.Hk * gdn::kDim * 2);
   m.v_bytes = round_up((size_t)m.s.T * m.s.Hv * gdn::kDim * 2);
-  m.total = m.chunk_bytes + 2 * m.q_bytes + 2 * m.v_bytes;
+  m.part_bytes = round_up((size_t)m.s.T * m.s.Hv * gdn::kDvTiles * 4);  // fused norm's row sums
+  m.total = m.chunk_bytes + 2 * m.q_bytes + 2 * m.v_bytes + m.part_bytes;
   return GDN_OK;
+}
+
+// Whether the mixer's gated RMSNorm can run fused into the state pass: every work item in one round
+// of resident workgroups (no persistent walk, no time split) and cooperative launch available.
+std::atomic<int> g_coop[kMaxDevices];  // 0 unknown, 1 yes, 2 no
+bool fused_norm_ok(const Shape &s, hipStream_t stream) {
+  if (s.T <= 0) return false;
+  const int groups = device_max_groups(stream);
+  if ((int64_t)s.N * s.Hv * gdn::kDvTiles > groups || plan_split(s, groups).segs) return false;
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  int c = g_coop[dev].load(std::memory_order_relaxed);
+  if (!c) {
+    int coop = 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+    c = coop ? 1 : 2;
+    g_coop[dev].store(c, std::memory_order_relaxed);
+  }
+  return c == 1;
 }
 }  // namespace
 
@@ -417,11 +443,15 @@ size_t gdn_mixer_fwd_workspace_size(const gdn_mixer_desc *d) {
   return m.total;
 }
 
-int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
-                       const float *g, const float *beta, const void *z, const void *norm_w,
-                       const int32_t *cu_seqlens, const float *h0, const void *conv_in,
-                       int32_t num_states, const int32_t *state_index, void *y, float *hT,
-                       void *conv_out, void *stream) {
+}  // extern "C"
+
+namespace {
+// The mixer, with the gated RMSNorm as its own kernel after the state pass (fuse_norm false) or
+// fused into the state pass's output path (true; GDN_ERR_UNSUPPORTED where fused_norm_ok fails).
+int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
+              const float *beta, const void *z, const void *norm_w, const int32_t *cu_seqlens,
+              const float *h0, const void *conv_in, int32_t num_states, const int32_t *state_index,
+              void *y, float *hT, void *conv_out, void *stream, bool fuse_norm_requested) {
   MixerLayout m;
   int st = mixer_layout(d, m);
   if (st != GDN_OK) return st;
@@ -466,13 +496,19 @@ int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *con
   unsigned char *kp = qp + m.q_bytes;
   unsigned char *vp = kp + m.q_bytes;
   unsigned char *op = vp + m.v_bytes;
+  uint32_t *part = reinterpret_cast<uint32_t *>(op + m.v_bytes);
+  const bool fuse_norm = fuse_norm_requested && tok;
+  if (fuse_norm && !fused_norm_ok(s, strm)) return GDN_ERR_UNSUPPORTED;
+  const gdn::NormOut norm{static_cast<const unsigned short *>(z), static_cast<const unsigned short *>(norm_w),
+                          static_cast<unsigned short *>(y), part, d->norm_eps};
   (void)hipGetLastError();
   // With pairs of v-heads per k-head the chunk prep makes q, k, v from qkv itself (one kernel
   // instead of the input prep, then the chunk prep); otherwise the input prep runs first.
   const bool fused = tok && (s.Hv / s.Hk) % 2 == 0;
   if (fused) {
     gdn::launch_chunk_prep_conv(qkv, conv_w, conv_in, state_index, num_states, g, beta, cu_seqlens,
-                                s.T, s.N, s.Hk, s.Hv, s.nslots, base, qp, kp, vp, strm);
+                                s.T, s.N, s.Hk, s.Hv, s.nslots, base, qp, kp, vp,
+                                fuse_norm ? part : nullptr, strm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
   } else if (tok) {
@@ -489,21 +525,44 @@ int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *con
     if (e != hipSuccess) return record_hip(e);
   }
   const StatePool pool{h0, num_states, state_index};
-  st = run_chunk(s, fused ? kPass : kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm);
+  st = run_chunk(s, fused ? kPass : kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm,
+                 fuse_norm ? &norm : nullptr);
   if (st != GDN_OK) return st;
-  if (tok) {
+  if (tok && !fuse_norm) {
     gdn::launch_gated_rmsnorm(op, z, norm_w, d->norm_eps, s.T, s.Hv, y, strm);
     return record_hip(hipGetLastError());
   }
   return GDN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                       const float *g, const float *beta, const void *z, const void *norm_w,
+                       const int32_t *cu_seqlens, const float *h0, const void *conv_in,
+                       int32_t num_states, const int32_t *state_index, void *y, float *hT,
+                       void *conv_out, void *stream) {
+  return run_mixer(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, num_states, state_index, y,
+                   hT, conv_out, stream, false);
+}
+
 int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
                   const float *beta, const void *z, const void *norm_w,
                   const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream) {
   if (!d) return GDN_ERR_NULL;
-  return gdn_mixer_fwd_cont(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, nullptr,
-                            d->chunk.num_seqs, nullptr, y, hT, nullptr, stream);
+  return run_mixer(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, nullptr, d->chunk.num_seqs, nullptr,
+                   y, hT, nullptr, stream, false);
+}
+
+int gdn_mixer_fwd_fused_norm(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                             const float *g, const float *beta, const void *z, const void *norm_w,
+                             const int32_t *cu_seqlens, const float *h0, void *y, float *hT,
+                             void *stream) {
+  if (!d) return GDN_ERR_NULL;
+  return run_mixer(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, nullptr, d->chunk.num_seqs, nullptr,
+                   y, hT, nullptr, stream, true);
 }
 
 }  // extern "C"

@@ -59,6 +59,19 @@ struct SplitPass {
 // With a split, the state buffers hold at most kSplitStates (segment, v-head) states each.
 constexpr int kSplitStates = 32;
 
+// The mixer's gated RMSNorm fused into the state pass's output path: the pass writes
+// y = o / sqrt(mean_dv(o^2) + eps) * w * silu(z) per (token, v-head) instead of o.  A row's 128
+// columns are spread over the kDvTiles column workgroups of its head; each publishes its tile's
+// sum of squares of the bf16 row as one device-scope atomic word of part ([T, Hv, kDvTiles]),
+// which the chunk prep fills with kPartEmpty first, so every word is its own "written" flag.
+struct NormOut {
+  const unsigned short *z, *w;  // bf16 [T, Hv, 128], bf16 [128]
+  unsigned short *y;            // bf16 [T, Hv, 128]
+  uint32_t *part;
+  float eps;
+};
+constexpr uint32_t kPartEmpty = 0xffffffffu;
+
 // Chunk-slot numbering: chunk c of sequence n lives in slot cu[n] / 64 + n + c.  The map is
 // injective and monotone, and every slot index is below T / 64 + N.
 __host__ __device__ inline int64_t num_slots(int64_t T, int32_t N) { return T / kChunk + N; }

@@ -328,6 +328,87 @@ __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, i
   }
 }
 
+// ---- The gated RMSNorm fused into the output path (mixer; see NormOut) ------------------------
+// The rows leave the output waves in store_o's layout: lane i of lane group g holds row
+// 16 pw + 4 g + i % 4 of the chunk, columns 4 (i / 4) .. + 3 of the workgroup's 16, as bf16 -- the
+// rule's output at its rounding point.  Per chunk an output wave (norm_step) publishes its rows'
+// sums of squares over those 16 columns, issues the loads of the eight tile sums of the previous
+// chunk's rows, and finishes the chunk before that: waits, if it must, until all eight tile sums of
+// its rows are written, and stores y for its own 16 columns.  The other workgroups of the head walk
+// the same chunks at the same pace, so their sums are written about two chunks before they are
+// needed; the wait is bounded (kNormSpin) and only terminates early because the kernel is launched
+// cooperatively: every workgroup of the head is resident and progresses.  o never leaves the
+// workgroup, and the separate norm kernel's pass over o and z disappears.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kNormSpin = 1 << 22;  // sleeps of ~64 clocks: far beyond any in-order progress
+struct NormRow {
+  v4i16 o;   // bf16 o of the lane's row, 4 columns
+  u32x2 z;   // bf16 z of the same
+  int t;     // the row's token, -1 past the sequence end
+  int tl;    // a token of the same chunk that exists (t, or the chunk's first)
+};
+struct NormSums {
+  uint32_t a, b;  // tile sums 2 (i / 4) and 2 (i / 4) + 1 of the lane's row
+};
+__device__ __forceinline__ NormSums norm_load(const NormOut &no, const NormRow &r, int Hv, int h, int l) {
+  const uint32_t *p = no.part + ((size_t)r.tl * Hv + h) * kDvTiles + 2 * ((l & 15) >> 2);
+  return NormSums{__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                  __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+}
+// The row slice of chunk c staged by out_stage: publish its tile sum of squares, load its z.
+__device__ __forceinline__ NormRow norm_stage(int c, int tb, int te, int Hv, int h, int d0, int tile, int pw,
+                                              int l, const unsigned char *slot, const NormOut &no) {
+  const int g = l >> 4, i = l & 15;
+  NormRow r;
+  r.o = lds_read_tr16(slot + 8 * (16 * g + 4 * (i & 3) + (i >> 2)));
+  const int t0 = tb + kChunk * c, row = 16 * pw + 4 * g + (i & 3);
+  r.t = row < min(kChunk, te - t0) ? t0 + row : -1;
+  r.tl = r.t >= 0 ? r.t : t0;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = bits_to_float((unsigned short)r.o[e]);
+    ss += x * x;
+  }
+  ss += __shfl_xor(ss, 4, 64);  // the row's four lanes: i, i ^ 4, i ^ 8, i ^ 12
+  ss += __shfl_xor(ss, 8, 64);
+  uint32_t bits = __float_as_uint(ss);
+  if (bits == kPartEmpty) bits = 0x7fc00000u;  // a NaN sum must not read as "not yet written"
+  if (r.t >= 0 && (i >> 2) == 0)
+    __hip_atomic_store(no.part + ((size_t)r.t * Hv + h) * kDvTiles + tile, bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  r.z = *reinterpret_cast<const u32x2 *>(no.z + ((size_t)r.tl * Hv + h) * kDim + d0 + 4 * (i >> 2));
+  return r;
+}
+// y of a staged row slice from the eight tile sums of its row (loaded as sm).
+template <bool kNt>
+__device__ __forceinline__ void norm_finish(const NormRow &r, NormSums sm, u32x2 wv, int Hv, int h, int d0,
+                                            int l, const NormOut &no) {
+  bool empty = sm.a == kPartEmpty || sm.b == kPartEmpty;
+  for (int it = 0; __any(empty) && it < kNormSpin; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    sm = norm_load(no, r, Hv, h, l);
+    empty = sm.a == kPartEmpty || sm.b == kPartEmpty;
+  }
+  float ss = __uint_as_float(sm.a) + __uint_as_float(sm.b);
+  ss += __shfl_xor(ss, 4, 64);
+  ss += __shfl_xor(ss, 8, 64);
+  const float rn = rsqrt_hw(ss * (1.f / kDim) + no.eps);
+  float yv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned short zb = (unsigned short)(r.z[e >> 1] >> (16 * (e & 1)));
+    const unsigned short wb = (unsigned short)(wv[e >> 1] >> (16 * (e & 1)));
+    yv[e] = bits_to_float((unsigned short)r.o[e]) * rn * bits_to_float(wb) * silu(bits_to_float(zb));
+  }
+  if (r.t >= 0) {
+    u32x2 *dst = reinterpret_cast<u32x2 *>(no.y + ((size_t)r.t * Hv + h) * kDim + d0 + 4 * ((l & 15) >> 2));
+    const u32x2 val = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
+    if (kNt) __builtin_nontemporal_store(val, dst);
+    else *dst = val;
+  }
+}
+
 // The output path o = e^G o (Q H) + P U~ for row block w of a chunk, on the output wave that
 // shares a SIMD with compute wave w.  It issues no global->LDS loads: a wave's LDS reads wait for
 // its own global->LDS loads still in flight, which would tie these reads to load latency.  out_qh
@@ -611,14 +692,15 @@ __device__ __forceinline__ void next_item_copying(Walker &W, const Grid &g, cons
 
 }  // namespace
 
-// One item per workgroup (launches whose items all fit on the device at once).
-template <bool kONt>
+// One item per workgroup (launches whose items all fit on the device at once).  kNorm: the
+// mixer's gated RMSNorm fused into the output path (y instead of o; cooperative launch only).
+template <bool kONt, bool kNorm>
 __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const float *h0, const int32_t *__restrict__ h0_index, int num_h0,
     unsigned short *__restrict__ o, float *hT,  // hT may equal h0 when h0_index is NULL
-    const uint8_t *__restrict__ rec, int Hk, int Hv, SplitPass sp) {
+    const uint8_t *__restrict__ rec, int Hk, int Hv, SplitPass sp, NormOut no) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
@@ -703,6 +785,20 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
       PFrags pf;
       load_p(pf, rec_at(rec, slot0, h, Hv), ow, l);
       f32x4 O = zero4();
+      // fused norm: row slices of the previous chunk (na) and the one before (nb), and the tile
+      // sums of na's rows loaded one step before their use
+      NormRow na{}, nb{};
+      NormSums sb{};
+      u32x2 wv{};
+      if constexpr (kNorm) wv = *reinterpret_cast<const u32x2 *>(no.w + d0 + 4 * ((l & 15) >> 2));
+      auto norm_step = [&](int cc) {  // chunk cc staged; cc - 1 loads its sums; cc - 2 finishes
+        const NormRow nr = norm_stage(cc, tb, te, Hv, h, d0, tile, ow, l, oslot, no);
+        const NormSums s_new = norm_load(no, na, Hv, h, l);
+        if (cc >= 2) norm_finish<kONt>(nb, sb, wv, Hv, h, d0, l, no);
+        nb = na;
+        sb = s_new;
+        na = nr;
+      };
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
         if (c > 0) {
@@ -710,13 +806,23 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
           load_p(pf, rec_at(rec, slot0 + c, h, Hv), ow, l);
         }
         __syncthreads();  // b1
-        if (c > 0 && write_o) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+        if constexpr (kNorm) {
+          if (c > 0) norm_step(c - 1);
+        } else {
+          if (c > 0 && write_o) store_o<kONt>(c - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+        }
         O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
         __syncthreads();  // b3
       }
       out_stage(O, pf, decs + ((nc - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
-      if (write_o) store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+      if constexpr (kNorm) {
+        norm_step(nc - 1);
+        if (nc >= 2) norm_finish<kONt>(nb, sb, wv, Hv, h, d0, l, no);  // chunk nc - 2
+        norm_finish<kONt>(na, norm_load(no, na, Hv, h, l), wv, Hv, h, d0, l, no);  // chunk nc - 1
+      } else {
+        if (write_o) store_o<kONt>(nc - 1, tb, te, Hv, ow, l, oslot, ob, ooff);
+      }
     }
     return;
   }
@@ -1096,10 +1202,10 @@ void launch_state_scan(const float *phi, const float *bend, const float *h0, con
                      h0, h0_index, num_h0, hs, segs, Hv);
 }
 
-void launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
-                       const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
-                       const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
-                       hipStream_t stream, SplitPass sp) {
+hipError_t launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
+                             const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
+                             const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
+                             hipStream_t stream, SplitPass sp, const NormOut *norm) {
   // Items: N Hv 8 (a multiple of 8).  One round when they fit on the device at one workgroup per
   // CU (max_groups, a multiple of 8), else max_groups persistent workgroups.
   const int total = (sp.segs ? sp.segs : N) * Hv * kDvTiles;
@@ -1110,14 +1216,27 @@ void launch_state_pass(const void *q, const void *k, const void *v, const int32_
   const unsigned short *v16 = static_cast<const unsigned short *>(v);
   unsigned short *o16 = static_cast<unsigned short *>(o);
   const uint8_t *r8 = static_cast<const uint8_t *>(rec);
+  if (norm) {
+    // every workgroup of a head must be resident for the fused norm's waits to end: cooperative
+    // launch (the host plans this only for a single round without a time split)
+    if (G != total || sp.segs) return hipErrorInvalidValue;
+    NormOut no = *norm;
+    void *args[] = {&q16, &k16, &v16, (void *)&cu, (void *)&h0, (void *)&h0_index, &num_h0, &o16, &hT,
+                    &r8, &Hk, &Hv, &sp, &no};
+    const void *fn = o_nt ? reinterpret_cast<const void *>(&state_pass_kernel<true, true>)
+                          : reinterpret_cast<const void *>(&state_pass_kernel<false, true>);
+    return hipLaunchCooperativeKernel(fn, dim3(G), dim3(kThreads), args, 0, stream);
+  }
+  const NormOut none{};
   if (G == total)
-    hipLaunchKernelGGL(o_nt ? state_pass_kernel<true> : state_pass_kernel<false>, dim3(G),
+    hipLaunchKernelGGL((o_nt ? state_pass_kernel<true, false> : state_pass_kernel<false, false>), dim3(G),
                        dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0, o16, hT,
-                       r8, Hk, Hv, sp);
+                       r8, Hk, Hv, sp, none);
   else
     hipLaunchKernelGGL(o_nt ? state_pass_multi_kernel<true> : state_pass_multi_kernel<false>,
                        dim3(G), dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0,
                        o16, hT, r8, Hk, Hv, total);
+  return hipGetLastError();
 }
 
 }  // namespace gdn

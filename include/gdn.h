@@ -219,6 +219,25 @@ GDN_EXPORT int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const voi
                   const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream);
 
 /*
+ * gdn_mixer_fwd with the gated RMSNorm fused into the state pass's output path instead of run as a
+ * kernel of its own (the "open-jev-fast" README, "Phase 3" item 4, measured this fusion on B300 and
+ * kept the separate kernel).  Each of a head's column workgroups publishes its share of every
+ * row's sum of squares and, a few chunks later, writes y for its own columns, so o never goes to
+ * memory.  That needs every workgroup of a head resident at once: the state pass is launched
+ * cooperatively, so this entry point returns GDN_ERR_UNSUPPORTED (nothing launched) when the work
+ * items do not fit on the device in one round (N * Hv * 8 above the device's concurrent
+ * workgroups), when one long sequence would take the time split, or when the device has no
+ * cooperative launch.  Arguments, workspace (gdn_mixer_fwd_workspace_size) and tolerances are
+ * gdn_mixer_fwd's; y can differ from it in the last bf16 bit (the row's sum of squares is added in
+ * another order).  Measured on MI355X at T = 936, Hk = 16, Hv = 32 (48 layers): 97 us per layer
+ * against 43 us for gdn_mixer_fwd, so gdn_mixer_fwd keeps the separate norm kernel.
+ */
+GDN_EXPORT int gdn_mixer_fwd_fused_norm(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                                        const float *g, const float *beta, const void *z,
+                                        const void *norm_w, const int32_t *cu_seqlens,
+                                        const float *h0, void *y, float *hT, void *stream);
+
+/*
  * The mixer continuing from carried states: beside the recurrent state, each sequence carries
  * the conv input window -- the last conv_taps - 1 rows of qkv before it -- so that both can pass
  * from a prefix to the candidates that continue it (the "open-jev-fast" README, "Phase 2" item 2,

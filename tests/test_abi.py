@@ -146,18 +146,24 @@ def test_workspace_alias_with_input():
     assert _call(desc=gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["k"], ws)) == gdn.GDN_ERR_ALIAS
 
 
-def test_mixer_validation():
+@pytest.mark.parametrize("entry", ["gdn_mixer_fwd", "gdn_mixer_fwd_fused_norm"])
+def test_mixer_validation(entry):
+    # the fused-norm entry point checks its arguments exactly as gdn_mixer_fwd does, before it looks
+    # at the device (whether the work fits in one round) or launches anything
     a = _addrs()
     ws = gdn.gdn_mixer_fwd_workspace_size(T, N, HK, HV)
     P = ctypes.c_void_p
+    fn = getattr(gdn.lib(), entry)
 
     def call(m, **over):
         b = {"qkv": a["q"], "cw": a["k"], "g": a["g"], "beta": a["beta"], "z": a["v"], "nw": a["h0"] + GB // 2,
              "cu": a["cu"], "h0": a["h0"], "y": a["o"], "hT": a["hT"]}
         b.update(over)
         pp = lambda x: None if x is None else P(x)
-        return gdn.lib().gdn_mixer_fwd(ctypes.byref(m), pp(b["qkv"]), pp(b["cw"]), pp(b["g"]), pp(b["beta"]), pp(b["z"]),
-                                       pp(b["nw"]), pp(b["cu"]), pp(b["h0"]), pp(b["y"]), pp(b["hT"]), None)
+        return fn(ctypes.byref(m) if m is not None else None, pp(b["qkv"]), pp(b["cw"]), pp(b["g"]), pp(b["beta"]),
+                  pp(b["z"]), pp(b["nw"]), pp(b["cu"]), pp(b["h0"]), pp(b["y"]), pp(b["hT"]), None)
+
+    assert call(None) == gdn.GDN_ERR_NULL
 
     good = lambda taps=4, eps=1e-6, wsb=ws: gdn.MixerDesc(gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], wsb), taps, eps)
     assert call(good(taps=3)) == gdn.GDN_ERR_UNSUPPORTED

@@ -13,11 +13,11 @@ from tests.gpu_util import bf16_dev, f32_dev, rel_l2, say
 pytestmark = pytest.mark.gpu
 
 
-def run_mixer_gpu(m: gi.MixerInputs, Hk=16, Hv=32):
+def run_mixer_gpu(m: gi.MixerInputs, Hk=16, Hv=32, fused_norm=False):
     y, hT = gdn.gdn_mixer_fwd(bf16_dev(m.qkv), bf16_dev(m.conv_w), f32_dev(m.g), f32_dev(m.beta), bf16_dev(m.z),
                               bf16_dev(m.norm_w), torch.from_numpy(m.cu.astype(np.int32)).cuda(),
                               None if m.h0 is None else f32_dev(m.h0), Hk=Hk, Hv=Hv,
-                              cu_seqlens_host=torch.from_numpy(m.cu.astype(np.int64)))
+                              cu_seqlens_host=torch.from_numpy(m.cu.astype(np.int64)), fused_norm=fused_norm)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), hT.cpu().numpy().astype(np.float64)
 
@@ -63,10 +63,52 @@ def check_mixer(y, hT, y_ref, h_ref, o_ref, tag, m: gi.MixerInputs):
     assert ry <= 5e-3 and worst <= 1.0 and rh <= 1e-3
 
 
+def pure_fp64_errors(y, hT, m: gi.MixerInputs, tag, Hk=16, Hv=32):
+    """Printed, not asserted: the GPU's y and hT against the mixer in fp64 throughout, without the bf16
+    rounding points of the prepped q, k, v and of o that the asserted oracle keeps (the GPU path has
+    them by construction: its chunk path takes bf16 q, k, v and writes bf16 o)."""
+    f = gi.bits_to_f64
+    h0 = None if m.h0 is None else m.h0.astype(np.float64)
+    y64, h64 = oracle.mixer_fwd(f(m.qkv), f(m.conv_w), m.g.astype(np.float64), m.beta.astype(np.float64), f(m.z),
+                                f(m.norm_w), m.cu.astype(np.int64), h0, Hk=Hk, Hv=Hv, bf16_points=False)
+    say(f"  {tag} vs the pure-fp64 mixer (not asserted): y rel-L2 {rel_l2(y, y64):.3e} | hT rel-L2 {rel_l2(hT, h64):.3e}")
+
+
 def test_mixer_t936_layer0():
     say("[mixer] T=936 Hk=16 Hv=32 seed=100")
     m = gi.make_mixer_inputs(100)
-    check_mixer(*run_mixer_gpu(m), *run_mixer_oracle(m), "T=936", m)
+    y, hT = run_mixer_gpu(m)
+    check_mixer(y, hT, *run_mixer_oracle(m), "T=936", m)
+    pure_fp64_errors(y, hT, m, "T=936")
+
+
+@pytest.mark.parametrize("case", ["t936", "varlen"])
+def test_mixer_fused_norm(case):
+    # gdn_mixer_fwd_fused_norm: the gated RMSNorm inside the state pass.  Same tolerances as the
+    # separate kernel; hT bitwise equal to gdn_mixer_fwd (the norm does not touch it); y equal up to
+    # the order of the row's sum of squares.
+    if case == "t936":
+        m, Hk, Hv = gi.make_mixer_inputs(100), 16, 32
+    else:
+        m, Hk, Hv = gi.make_mixer_inputs(7, lengths=[5, 70, 3, 130, 1], Hk=2, Hv=4, with_h0=True), 2, 4
+    say(f"[mixer-fused-norm] {case} Hk={Hk} Hv={Hv} T={m.qkv.shape[0]}")
+    y, hT = run_mixer_gpu(m, Hk, Hv, fused_norm=True)
+    y_sep, h_sep = run_mixer_gpu(m, Hk, Hv)
+    assert np.array_equal(hT, h_sep), "hT differs from gdn_mixer_fwd"
+    say(f"  y against gdn_mixer_fwd: rel-L2 {rel_l2(y, y_sep):.3e} max|d| {np.abs(y - y_sep).max():.3e}")
+    check_mixer(y, hT, *run_mixer_oracle(m, Hk, Hv), f"fused norm {case}", m)
+    pure_fp64_errors(y, hT, m, f"fused norm {case}", Hk, Hv)
+
+
+@pytest.mark.parametrize("lengths,Hk,Hv", [([40] * 40, 2, 4), ([3000], 1, 4)])
+def test_mixer_fused_norm_unsupported(lengths, Hk, Hv):
+    # 40 sequences x 4 v-heads x 8 tiles take more than one round of workgroups; one sequence of
+    # 3000 tokens at Hv = 4 takes the time split: neither is launched fused (nothing is enqueued).
+    say(f"[mixer-fused-norm] unsupported: {len(lengths)} x {lengths[0]} Hk={Hk} Hv={Hv}")
+    m = gi.make_mixer_inputs(9, lengths=lengths, Hk=Hk, Hv=Hv)
+    with pytest.raises(gdn.GdnError) as e:
+        run_mixer_gpu(m, Hk, Hv, fused_norm=True)
+    assert e.value.code == gdn.GDN_ERR_UNSUPPORTED
 
 
 def test_mixer_varlen_conv_resets_with_h0():
