@@ -23,9 +23,10 @@
 //      the column's blocks kept in registers, one wave per block column (no barrier in between).
 //   5. T' = T diag(beta) as bf16 hi + lo MFMA fragments, e^{G} and e^{G_last - G}: the rest of the
 //      record the state pass reads.
-// The record is written with streaming (non-temporal) stores: only the next kernel reads it, often
-// from another XCD, so it should be in memory when this kernel ends rather than written back from
-// L2 at the kernel boundary.
+// The record's T' fragments and decays are written with streaming (non-temporal) stores: only the
+// next kernel reads them, often from another XCD, so they should be in memory when this kernel ends
+// rather than written back from L2 at the kernel boundary; P, whose lanes are written in two
+// halves, goes through L2.
 // Every exponent is <= 0 (G is non-increasing), so no e^{-G} is ever formed.  Tokens past the
 // end of a sequence enter as k = q = 0, g = 0, beta = 0, which leaves T' and P zero on them.
 #include "gdn_device.h"
@@ -370,11 +371,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
           const u32x2 val = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
           uint8_t *dst = rec_slot + (size_t)(h_first + x) * kRecBytes + kRecP +
                          frag_index(rb, cb >> 1) * kFragBytes + l * 16 + 8 * (cb & 1);
+          // Cached stores: the two 8-byte halves of a lane's 16 bytes come from different waves and
+          // merge in L2 before the line goes to memory (streaming stores would send each half-line
+          // on its own: 23 MB more written at T = 16,384).
           if ((cb & 1) == 0 && cb + 1 > rb) {  // the other half is an upper block: zeros
             const u32x4 v4 = {val[0], val[1], 0u, 0u};
-            __builtin_nontemporal_store(v4, reinterpret_cast<u32x4 *>(dst));
+            *reinterpret_cast<u32x4 *>(dst) = v4;
           } else {
-            __builtin_nontemporal_store(val, reinterpret_cast<u32x2 *>(dst));
+            *reinterpret_cast<u32x2 *>(dst) = val;
           }
         } else {
           float *Ax = reinterpret_cast<float *>(smem + kOffA + x * kMatBytes);
