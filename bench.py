@@ -226,6 +226,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warmup steps, repeat the step for this long (untimed) so that the "
+                         "GPU clock has left its idle state; reported as timing.settle_*")
     ap.add_argument("--workload", default="t16384_h16x32")
     ap.add_argument("--rotate-mib", type=float, default=512.0,
                     help="rotate among input copies until their footprint exceeds this (cold caches)")
@@ -312,7 +315,21 @@ def main():
         tokens_per_step = T * LAYERS
         layers_per_step = LAYERS
 
-    # ---- warmup + timed region ----------------------------------------------------------------
+    # ---- clock settling, warmup, timed region --------------------------------------------------
+    # A GPU that has been idle starts a run at a lower clock and reaches its sustained clock only
+    # after some tens of milliseconds of load (T = 16,384: 414 us per step over the first 25 steps,
+    # 350 us over 200).  The step is therefore repeated, untimed, for --settle-ms first; the warmup
+    # steps and the exactly --steps timed steps follow.
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while True:
+        step(settle_steps)
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t_settle) * 1e3 >= args.settle_ms:
+                break
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -434,7 +451,9 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg,
             "roofline": roofline, "cpu_baseline": cpu, "path_roofline": path, "stages": stages,
-            "parity": parity, "device": {"name": props.name, "cus": props.multi_processor_count}}
+            "parity": parity, "device": {"name": props.name, "cus": props.multi_processor_count},
+            "timing": {"settle_ms": round(settle_ms, 1), "settle_steps": settle_steps,
+                       "note": "untimed steps before the warmup steps, until the GPU clock has settled"}}
     print(json.dumps(line), flush=True)
 
 
