@@ -125,8 +125,6 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin (hardware id b runs on XCD b % 8).  Renumber
-// so that consecutive logical ids share an XCD and therefore its L2.
 // ---- GDN mixer input prep (conv + SiLU + L2 norm): shared by mixer_prep_kernel and the prep
 // kernel that makes q, k, v from the packed input itself ----
 // x sigmoid(x) with the hardware exp2 and reciprocal (each about 1 ulp): the result is rounded
@@ -155,7 +153,8 @@ __device__ __forceinline__ const unsigned short *window_of(const unsigned short 
   return (r >= 0 && r < num_states) ? conv_in + (size_t)r * rows : nullptr;
 }
 
-
+// Workgroups are dealt to the 8 XCDs round-robin (hardware id b runs on XCD b % 8).  Renumber
+// so that consecutive logical ids share an XCD and therefore its L2.
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
   if (nblocks % 8 != 0) return bid;
   return (bid % 8) * (nblocks / 8) + bid / 8;
