@@ -25,7 +25,12 @@
 //   phase 2: compute waves: U~ = T' R (K^T fragments read behind it); U~ (decayed
 //            hi/lo and plain) to LDS
 //            output waves:  the previous chunk's rows to memory; Q H                 -> b2
-//   phase 3: compute waves: H update, H (bf16 hi and lo) to LDS                      -> b3
+//   phase 3: compute waves: H update, H (bf16 hi and lo) to LDS; the next chunk's K rows
+//            output waves:  the LDS operands of this chunk's P U~                    -> b3
+// Phase 1 ends on the output waves and carries the most LDS traffic, phase 3 the least: the
+// reads of phase 3 that are not needed until phase 1 take LDS load off phase 1 (measured: 2-3 %
+// off the pass at T = 16,384; reading everything of a phase at once, before its first product,
+// was slower).
 // so the output path of chunk c finishes during chunk c + 1, off the chunk's last barrier (the
 // persistent kernel runs it between b2 and b3 of chunk c instead; see there).
 // Thirteen waves per workgroup:
@@ -169,6 +174,8 @@ static_assert(kRecTpLo == kRecTpHi + kTpBytes / 2 && kDmaTp % 4 == 0, "T' hi | l
 // Producer wave kDecWave also loads the chunk's decays (one half-wave instruction).
 constexpr int kDecWave = 1;
 __host__ __device__ constexpr int kChunkCount(int pw) { return kTileCount(pw) + (pw == kDecWave ? 1 : 0); }
+// Loads every producer wave issues in parts 0 and 1 of a chunk (one T' KiB and four tile rows each).
+constexpr int kPartsBeforeB2 = 2 * (1 + 4);
 
 // Per-lane byte offsets of a producer wave's loads, fixed for the whole sequence.  Tile
 // instruction i of wave pw covers tile rows 16 i + 4 pw .. + 3 (lane l: row 16 i + 4 pw + l / 16,
@@ -427,16 +434,36 @@ __device__ __forceinline__ f32x4 out_qh(const unsigned char *qt, const unsigned 
                   lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), O);
   return O;
 }
-__device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const unsigned char *ds,
-                                          const unsigned char *Uo, int w, int l,
-                                          unsigned char *oslot) {
+// The LDS operands of out_stage for row block w: e^G of its rows and the B operands of P U~.
+struct OutOps {
+  f32x4 eg;
+  bf16x8 u[2];
+};
+__device__ __forceinline__ OutOps out_fetch(const unsigned char *ds, const unsigned char *Uo, int w, int l) {
   const int lj = l & 15, lg = l >> 4;
-  const f32x4 eg = *reinterpret_cast<const f32x4 *>(ds + kDecEG + (16 * w + 4 * lg) * 4);
+  OutOps r;
+  r.eg = *reinterpret_cast<const f32x4 *>(ds + kDecEG + (16 * w + 4 * lg) * 4);
+  r.u[0] = lds_bf16x8(Uo + pmaj(lj, 4 * lg));
+  r.u[1] = w >= 2 ? lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)) : r.u[0];
+  return r;
+}
+__device__ __forceinline__ void out_stage(f32x4 O, const PFrags &r, const OutOps &x, int w, int l,
+                                          unsigned char *oslot) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) O[rr] *= eg[rr];
-  O = mfma_bf16(r.p[0], lds_bf16x8(Uo + pmaj(lj, 4 * lg)), O);
-  if (w >= 2) O = mfma_bf16(r.p[1], lds_bf16x8(Uo + pmaj(lj, 32 + 4 * lg)), O);
+  for (int rr = 0; rr < 4; ++rr) O[rr] *= x.eg[rr];
+  O = mfma_bf16(r.p[0], x.u[0], O);
+  if (w >= 2) O = mfma_bf16(r.p[1], x.u[1], O);
   store_u32x2(oslot + 8 * l, pack_bf16x2(O[0], O[1]), pack_bf16x2(O[2], O[3]));
+}
+
+// Compute wave w's K rows 16 w .. 16 w + 15 of the tile in ring slot ts, as the A operands of
+// X = K H: ka[ks][p] holds keys 32 ks + 64 p + 8 lg .. + 7 in lane group lg.
+__device__ __forceinline__ void read_k_rows(bf16x8 (&ka)[2][2], const unsigned char *ts, int w, int l) {
+  const int lj = l & 15, lg = l >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) ka[ks][p] = lds_bf16x8(ts + kTK + swz(16 * w + lj, 32 * ks + 64 * p + 8 * lg));
 }
 
 // This wave's state slice into the H exchange buffers as bf16 hi (Ht) and lo (Htl = bf16(H - hi)):
@@ -456,14 +483,18 @@ __device__ __forceinline__ void write_ht(unsigned char *Ht, unsigned char *Htl, 
 }
 
 // One chunk on compute wave w: tile ring slot ts (K, Q, V tiles and T' fragments), decay ring
-// slot ds.  Rows past the sequence end hold clamped data; they need no masking because T' has
+// slot ds.  ka holds this wave's K rows of the chunk (the A operands of X = K H), read during the
+// previous step; once the step has read U~ it reads those of the next chunk from slot tsn (landed
+// by b2, see the producers), so that phase 1 -- the step's LDS-heaviest -- reads only H, V and
+// the decays.  Rows past the sequence end hold clamped data; they need no masking because T' has
 // zero rows and columns there (beta = 0), so U~ is zero on them, and their output rows are never
 // stored.  The output path runs on the output waves (out_qh, out_stage).  With kWriteHt the step
 // ends with the bf16 copy of the new state in the exchange buffer and the chunk's last barrier (b3);
 // without it the caller does both, after any change of H between items.
 template <bool kWriteHt>
-__device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *ds, int w,
-                                           int l, f32x4 (&H)[2], unsigned char *Ht,
+__device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsigned char *tsn,
+                                           const unsigned char *ds, int w, int l, bf16x8 (&ka)[2][2],
+                                           f32x4 (&H)[2], unsigned char *Ht,
                                            unsigned char *Htl, unsigned char *Rh, unsigned char *Rl,
                                            unsigned char *Uh, unsigned char *Ul, unsigned char *Uo,
                                            bool zero_v = false) {
@@ -474,12 +505,10 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
   f32x4 X = zero4(), X2 = zero4();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 a0 = lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 8 * lg));
-    const bf16x8 a1 = lds_bf16x8(kt + swz(16 * w + lj, 32 * ks + 64 + 8 * lg));
-    X = mfma_bf16(a0, lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), X);
-    X2 = mfma_bf16(a1, lds_bf16x8(Ht + vmaj(lj, 32 * ks + 64 + 8 * lg)), X2);
-    X = mfma_bf16(a0, lds_bf16x8(Htl + vmaj(lj, 32 * ks + 8 * lg)), X);
-    X2 = mfma_bf16(a1, lds_bf16x8(Htl + vmaj(lj, 32 * ks + 64 + 8 * lg)), X2);
+    X = mfma_bf16(ka[ks][0], lds_bf16x8(Ht + vmaj(lj, 32 * ks + 8 * lg)), X);
+    X2 = mfma_bf16(ka[ks][1], lds_bf16x8(Ht + vmaj(lj, 32 * ks + 64 + 8 * lg)), X2);
+    X = mfma_bf16(ka[ks][0], lds_bf16x8(Htl + vmaj(lj, 32 * ks + 8 * lg)), X);
+    X2 = mfma_bf16(ka[ks][1], lds_bf16x8(Htl + vmaj(lj, 32 * ks + 64 + 8 * lg)), X2);
   }
   X += X2;
   const f32x4 eg = *reinterpret_cast<const f32x4 *>(ds + kDecEG + (16 * w + 4 * lg) * 4);
@@ -554,17 +583,23 @@ __device__ __forceinline__ void chunk_step(const unsigned char *ts, const unsign
   }
   __syncthreads();
 
-  // H = e^{G_last} H + K^T (e^{G_last - G} o U~)  (decayed U~ hi + lo)
+  // H = e^{G_last} H + K^T (e^{G_last - G} o U~)  (decayed U~ hi + lo); the next chunk's K rows
+  // are read behind U~.
+  bf16x8 bh[2], bl[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bh[ks] = lds_bf16x8(Uh + vmaj(lj, 32 * ks + 8 * lg));
+    bl[ks] = lds_bf16x8(Ul + vmaj(lj, 32 * ks + 8 * lg));
+  }
+  read_k_rows(ka, tsn, w, l);
 #pragma unroll
   for (int a = 0; a < 2; ++a) H[a] *= egc;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 bh = lds_bf16x8(Uh + vmaj(lj, 32 * ks + 8 * lg));
-    const bf16x8 bl = lds_bf16x8(Ul + vmaj(lj, 32 * ks + 8 * lg));
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      H[a] = mfma_bf16(kc[a][ks], bh, H[a]);
-      H[a] = mfma_bf16(kc[a][ks], bl, H[a]);
+      H[a] = mfma_bf16(kc[a][ks], bh[ks], H[a]);
+      H[a] = mfma_bf16(kc[a][ks], bl[ks], H[a]);
     }
   }
   if constexpr (kWriteHt) {
@@ -799,10 +834,11 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         sb = s_new;
         na = nr;
       };
+      OutOps oo;  // LDS operands of chunk c's P U~, read in phase 3 of chunk c (LDS is lightly used there)
       __syncthreads();
       for (int c = 0; c < nc; ++c) {
         if (c > 0) {
-          out_stage(O, pf, decs + ((c - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
+          out_stage(O, pf, oo, ow, l, oslot);
           load_p(pf, rec_at(rec, slot0 + c, h, Hv), ow, l);
         }
         __syncthreads();  // b1
@@ -813,9 +849,10 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         }
         O = out_qh(tiles + (c % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
+        oo = out_fetch(decs + (c % kDecStages) * kDecBytes, Uo, ow, l);
         __syncthreads();  // b3
       }
-      out_stage(O, pf, decs + ((nc - 1) % kDecStages) * kDecBytes, Uo, ow, l, oslot);
+      out_stage(O, pf, oo, ow, l, oslot);
       if constexpr (kNorm) {
         norm_step(nc - 1);
         if (nc >= 2) norm_finish<kONt>(nb, sb, wv, Hv, h, d0, l, no);  // chunk nc - 2
@@ -862,14 +899,13 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
         dma_tiles<0>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
         dma_barrier();  // b1
         dma_tiles<1>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
+        // Chunk c + 1 (loaded during chunk c - 1) must have landed before b2, after which the
+        // compute waves read its K tile: loads complete in issue order, so it is enough that at
+        // most this iteration's loads so far are in flight.
+        wait_vmcnt<kPartsBeforeB2>();
         dma_barrier();  // b2
         dma_tiles<2>(cn, tb, te, Hk, Hv, pw, l, kb, qb, vb, tp, pl, tslot);
         if (pw == kDecWave) dma_dec(slot0 + cn, h, Hv, l, rec, decs_lds + ((c + 2) % kDecStages) * kDecBytes);
-        // Chunk c + 1 (loaded during chunk c - 1) must have landed before b3: loads complete in
-        // issue order, so it is enough that at most this iteration's loads are in flight.
-        if (pw == 3) wait_vmcnt<kChunkCount(3)>();
-        else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
-        else wait_vmcnt<kChunkCount(0)>();
         dma_barrier();  // b3
       }
     }
@@ -899,6 +935,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   if (nc > 0) {
     write_ht(Ht, Htl, H, w, l);
     __syncthreads();
+    bf16x8 ka[2][2];
+    read_k_rows(ka, tiles, w, l);
     // Unrolled over twice the period of the ring slots (3), so every slot address is a
     // compile-time offset rather than per-chunk address arithmetic on the compute waves (a
     // three-chunk body keeps more values live across its steps and spills).
@@ -907,8 +945,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
         if (c0 + u < nc)
-          chunk_step<true>(tiles + (u % 3) * kTileBytes, decs + (u % 3) * kDecBytes, w, l, H, Ht, Htl, Rh,
-                           Rl, Uh, Ul, Uo, ident);
+          chunk_step<true>(tiles + (u % 3) * kTileBytes, tiles + ((u + 1) % 3) * kTileBytes,
+                           decs + (u % 3) * kDecBytes, w, l, ka, H, Ht, Htl, Rh, Rl, Uh, Ul, Uo, ident);
       }
     }
   }
@@ -1015,7 +1053,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         __syncthreads();  // b1
         const f32x4 O = out_qh(tiles + (s % kTileStages) * kTileBytes + kTQ, Ht, ow, l);
         __syncthreads();  // b2
-        out_stage(O, pf, decs + (s % kDecStages) * kDecBytes, Uo, ow, l, oslot);
+        out_stage(O, pf, out_fetch(decs + (s % kDecStages) * kDecBytes, Uo, ow, l), ow, l, oslot);
         const int c_ = cur.c, tb_ = cur.it.tb, te_ = cur.it.te, h_ = cur.it.h;
         next_step(cur, gr, cu);
         if (cur.valid) load_p(pf, rec_at(rec, cur.it.slot0 + cur.c, cur.it.h, Hv), ow, l);
@@ -1067,15 +1105,14 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         dma_tiles<0>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
         dma_barrier();  // b1
         dma_tiles<1>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
+        // Step s + 1 (loaded during step s - 1) must have landed before b2, after which the
+        // compute waves read its K tile: loads complete in issue order, so it is enough that at
+        // most this iteration's loads so far are in flight.
+        wait_vmcnt<kPartsBeforeB2>();
         dma_barrier();  // b2
         dma_tiles<2>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
         if (pw == kDecWave)
           dma_dec(ld.it.slot0 + ld.c, ld.it.h, Hv, l, rec, decs_lds + ((s + 2) % kDecStages) * kDecBytes);
-        // Step s + 1 (loaded during step s - 1) must have landed before b3: loads complete in
-        // issue order, so it is enough that at most this iteration's loads are in flight.
-        if (pw == 3) wait_vmcnt<kChunkCount(3)>();
-        else if (pw == kDecWave) wait_vmcnt<kChunkCount(kDecWave)>();
-        else wait_vmcnt<kChunkCount(0)>();
         dma_barrier();  // b3
         next_step(cur, gr, cu);
       }
@@ -1096,6 +1133,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   load_h0(H, cur.it, h0, h0_index, num_h0, Hv, d0, w, l);
   write_ht(Ht, Htl, H, w, l);
   __syncthreads();
+  bf16x8 ka[2][2];
+  read_k_rows(ka, tiles, w, l);
   for (int s = 0; cur.valid; ++s) {
     const bool last = cur.c == cur.it.nc - 1;
     Walker nx = cur;
@@ -1103,8 +1142,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       next_item(nx, gr, cu);  // the next item's initial state (copies of empty items come later)
       if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
     }
-    chunk_step<false>(tiles + (s % kTileStages) * kTileBytes, decs + (s % kDecStages) * kDecBytes, w,
-                      l, H, Ht, Htl, Rh, Rl, Uh, Ul, Uo);
+    chunk_step<false>(tiles + (s % kTileStages) * kTileBytes, tiles + ((s + 1) % kTileStages) * kTileBytes,
+                      decs + (s % kDecStages) * kDecBytes, w, l, ka, H, Ht, Htl, Rh, Rl, Uh, Ul, Uo);
     if (last) {
       store_ht(H, cur.it, hT, Hv, d0, w, l);
       next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
