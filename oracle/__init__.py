@@ -17,6 +17,9 @@ shares no code with it.
   ("open-jev-fast" README, "Phase 2", item 1); :func:`mixer_fwd_cont` also carries
   the conv input window in and out beside the recurrent state, so that a call
   continues where another stopped.
+* :func:`gates` -- the gate parameters g and beta from the layer's projections (the last
+  input-prep step the "open-jev-fast" README, "Phase 2" item 1, names; the pages give no
+  formula, so it follows the Mamba2-style gating of the Gated DeltaNet paper that README cites).
 * :mod:`oracle.brute` -- exact rational arithmetic for tiny cases.
 
 State layout: ``h0``/``hT`` are key-major ``[N, Hv, dk, dv]`` (``H = S^T``).
@@ -71,6 +74,8 @@ def load_library(path: str):
     lib.oracle_round_bf16_array.argtypes = [P, P, i64]
     lib.oracle_round_bf16_array.restype = None
     lib.oracle_mixer_fwd.restype = ctypes.c_int
+    lib.oracle_gates.argtypes = [i64, i32, P, P, P, P, P, P]
+    lib.oracle_gates.restype = None
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -204,6 +209,19 @@ def round_bf16(x, lib=None):
     out = np.empty_like(a)
     (lib or _load()).oracle_round_bf16_array(_ptr(a), _ptr(out), a.size)
     return out
+
+
+def gates(a, b, A_log, dt_bias, lib=None):
+    """Gate parameters in fp64: g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b), per token
+    and v-head.  a, b: [T, Hv]; A_log, dt_bias: [Hv].  Returns (g, beta), each [T, Hv]."""
+    a, b, A_log, dt_bias = (_f64(x) for x in (a, b, A_log, dt_bias))
+    if a.ndim != 2 or b.shape != a.shape or A_log.shape != (a.shape[1],) or dt_bias.shape != A_log.shape:
+        raise ValueError("gate shapes")
+    g = np.empty_like(a)
+    beta = np.empty_like(a)
+    (lib or _load()).oracle_gates(a.shape[0], a.shape[1], _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g),
+                                  _ptr(beta))
+    return g, beta
 
 
 def mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, Hk=16, Hv=32, dk=128, dv=128,

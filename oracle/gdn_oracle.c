@@ -37,6 +37,13 @@
  *       o = gated delta rule(q, k, v, g, beta)
  *       y = o / sqrt(mean(o^2) + eps_norm) * w_norm * z * sigmoid(z)
  *
+ *   Gate parameters (the last step the "open-jev-fast" README, "Phase 2" item 1, lists for the
+ *   GDN input prep; the pages give no formula, so this follows the gating of the Gated DeltaNet
+ *   paper the README cites, a Mamba2-style decay): per token t and v-head h, from the layer's
+ *   projections a, b and the per-head parameters A_log, dt_bias,
+ *       g    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])     (log-decay, <= 0)
+ *       beta = sigmoid(b[t,h])
+ *
  *   The model is bf16 and its fused prep / norm kernels keep the reference's bf16 rounding
  *   points ("open-jev-fast" README, "Phase 2" item 1).  With bf16_points != 0 the mixer rounds
  *   the prepped q, k, v and the rule's output o to bf16 (round to nearest, ties to even) at
@@ -345,4 +352,19 @@ int oracle_mixer_fwd(int64_t T, int32_t N, int32_t Hk, int32_t Hv, int32_t dk, i
   return oracle_mixer_fwd_cont(T, N, Hk, Hv, dk, dv, taps, eps_l2, eps_norm, bf16_points, qkv,
                                conv_w, g, beta, z, norm_w, cu, h0, NULL, N, NULL, y, hT, NULL,
                                nthreads);
+}
+
+/* softplus(x) = log(1 + e^x), without overflow for large x. */
+static double softplus(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+/* Gate parameters of a packed batch (see the header):  a, b : [T, Hv];  A_log, dt_bias : [Hv];
+ * g, beta : [T, Hv] out. */
+void oracle_gates(int64_t T, int32_t Hv, const double *a, const double *b, const double *A_log,
+                  const double *dt_bias, double *g, double *beta) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t h = 0; h < Hv; ++h) {
+      const int64_t i = t * Hv + h;
+      g[i] = -exp(A_log[h]) * softplus(a[i] + dt_bias[h]);
+      beta[i] = sigmoid(b[i]);
+    }
 }

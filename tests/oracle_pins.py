@@ -463,3 +463,43 @@ def pin_mixer_fanout(api):
 
 CONT_PINS = [pin_fanout_brute, pin_fanout_equals_gathered, pin_conv_window_numpy, pin_mixer_split_continuation,
              pin_mixer_fanout]
+
+
+# ------------------------------------------------------------------------------------------
+# Gate parameters: g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b) per token and v-head.
+# Each takes ``gates`` (signature of oracle.gates).
+# ------------------------------------------------------------------------------------------
+def pin_gates_closed_forms(gates):
+    # a + dt_bias = 0: softplus(0) = ln 2, so g = -exp(A_log) ln 2; b = 0: beta = 1/2 exactly
+    A_log = np.array([0.0, np.log(2.0), -1.5, 2.0])
+    dt = np.array([0.25, -3.0, 1.0, 0.0])
+    g, beta = gates(np.tile(-dt, (3, 1)), np.zeros((3, 4)), A_log, dt)
+    assert np.allclose(g, -np.exp(A_log) * np.log(2.0), rtol=1e-15, atol=0), "g at softplus(0)"
+    assert np.array_equal(beta, np.full((3, 4), 0.5)), "beta at b = 0"
+    # with A_log = dt_bias = 0: softplus(x) - softplus(-x) = x and sigmoid(x) + sigmoid(-x) = 1
+    x = np.random.default_rng(61).standard_normal((5, 4)) * 4.0
+    z4 = np.zeros(4)
+    gp, bp = gates(x, x, z4, z4)
+    gm, bm = gates(-x, -x, z4, z4)
+    assert np.allclose(gm - gp, x, rtol=0, atol=1e-13), "softplus(x) - softplus(-x) = x"
+    assert np.allclose(bp + bm, 1.0, rtol=0, atol=1e-15), "sigmoid(x) + sigmoid(-x) = 1"
+    assert np.all(gp < 0) and np.all((bp > 0) & (bp < 1)), "g < 0 < beta < 1"
+
+
+def pin_gates_library(gates):
+    # against numpy's logaddexp (softplus) and scipy's expit (sigmoid), with |x| up to 60
+    from scipy.special import expit
+    rng = np.random.default_rng(62)
+    T, Hv = 40, 6
+    a = rng.standard_normal((T, Hv)) * 3.0
+    b = rng.standard_normal((T, Hv)) * 3.0
+    a[0], b[0] = 60.0, -60.0
+    a[1], b[1] = -60.0, 60.0
+    A_log = rng.uniform(-1.0, 2.8, Hv)
+    dt = np.log(np.expm1(rng.uniform(1e-3, 0.1, Hv)))
+    g, beta = gates(a, b, A_log, dt)
+    assert np.allclose(g, -np.exp(A_log) * np.logaddexp(0.0, a + dt), rtol=1e-14, atol=1e-300), "g vs logaddexp"
+    assert np.allclose(beta, expit(b), rtol=1e-14, atol=1e-300), "beta vs expit"
+
+
+GATE_PINS = [pin_gates_closed_forms, pin_gates_library]

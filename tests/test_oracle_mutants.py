@@ -65,6 +65,11 @@ MUTANTS = {
     "window_out_shifted": [("const int64_t p = cu[n + 1] - (taps - 1) + j;", "const int64_t p = cu[n + 1] - taps + j;")],
     "window_out_drops_carried": [("else if (win) val =", "else if (0) val =")],
     "bf16_point_on_o_missing": [("for (int64_t e = 0; e < T * Cv; ++e) o[e] = oracle_round_bf16(o[e]);", ";")],
+    "gate_sign": [("g[i] = -exp(A_log[h]) *", "g[i] = exp(A_log[h]) *")],
+    "gate_A_log_not_exponentiated": [("g[i] = -exp(A_log[h]) *", "g[i] = -A_log[h] *")],
+    "gate_dt_bias_dropped": [("softplus(a[i] + dt_bias[h])", "softplus(a[i])")],
+    "gate_softplus_as_exp": [("return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));", "return exp(x);")],
+    "beta_not_sigmoid": [("beta[i] = sigmoid(b[i]);", "beta[i] = b[i];")],
 }
 
 
@@ -103,6 +108,11 @@ def test_mutant_is_caught(tmp_path, name):
             pin(oracle_api(lib))
         except (AssertionError, RuntimeError, ValueError):
             caught.append(pin.__name__)
+    for pin in P.GATE_PINS:
+        try:
+            pin(functools.partial(oracle.gates, lib=lib))
+        except (AssertionError, RuntimeError, ValueError):
+            caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
 
 
@@ -115,3 +125,5 @@ def test_unmutated_copy_passes(tmp_path):
         pin(functools.partial(oracle.conv_silu, lib=lib), functools.partial(oracle.mixer_fwd, lib=lib), fwd)
     for pin in P.CONT_PINS:
         pin(oracle_api(lib))
+    for pin in P.GATE_PINS:
+        pin(functools.partial(oracle.gates, lib=lib))

@@ -85,3 +85,8 @@ def test_plain_entry_points_equal_the_general_ones():
     y2, h2, _ = oracle.mixer_fwd_cont(m["qkv"], m["conv_w"], m["g"], m["beta"], m["z"], m["norm_w"], m["cu"],
                                       Hk=2, Hv=4, dk=8, dv=8)
     assert np.array_equal(y, y2) and np.array_equal(hT, h2)
+
+
+@pytest.mark.parametrize("pin", P.GATE_PINS, ids=lambda f: f.__name__)
+def test_gate_pin(pin):
+    pin(oracle.gates)
