@@ -31,7 +31,8 @@ Workloads (seeded, synthetic; see gdn_inputs.py):
     t256_h4, t539_h16x32, varlen7_t677_h0, t936_h16x32, t3399_h16x32
     t16384_h2x4      T=16384 at Hk=2, Hv=4: one GPU's share when the heads are split over 8 GPUs
     mixer_t936_x48   48 GDN mixer layers at T=936, Hk=16, Hv=32, one layer per seed
-                     (--fused-norm: gdn_mixer_fwd_fused_norm, the norm inside the state pass)
+                     (--fused-norm: gdn_mixer_fwd_fused_norm, the norm inside the state pass;
+                     --gates: gdn_mixer_fwd_gates, g and beta made from the projections)
 """
 from __future__ import annotations
 
@@ -84,9 +85,12 @@ def pass_bytes(T, N, Hk, Hv, nch, with_h0):
             + T * Hv * D * 2 + state * (2 if with_h0 else 1))
 
 
-def mixer_bytes(T, N, Hk, Hv):
+def mixer_bytes(T, N, Hk, Hv, gates=False):
+    """Algorithmic bytes of one mixer layer: qkv, conv weights, g and beta (fp32) or, with the gate
+    step, a and b (bf16) and A_log, dt_bias (fp32 per head), z, y, norm weight, hT."""
     C = (2 * Hk + Hv) * D
-    return T * C * 2 + C * 4 * 2 + T * Hv * 8 + T * Hv * D * 2 * 2 + D * 2 + N * Hv * D * D * 4
+    gate_bytes = T * Hv * 4 + Hv * 8 if gates else T * Hv * 8
+    return T * C * 2 + C * 4 * 2 + gate_bytes + T * Hv * D * 2 * 2 + D * 2 + N * Hv * D * D * 4
 
 
 # ------------------------------------------------------------------------------------------------
@@ -233,6 +237,8 @@ def main():
     ap.add_argument("--rotate-mib", type=float, default=512.0,
                     help="rotate among input copies until their footprint exceeds this (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gates", action="store_true",
+                    help="mixer workload: gate parameters from the projections (gdn_mixer_fwd_gates)")
     ap.add_argument("--fused-norm", action="store_true",
                     help="mixer workload: gated RMSNorm fused into the state pass (gdn_mixer_fwd_fused_norm)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on oracle time for the baseline")
@@ -301,6 +307,9 @@ def main():
             m = gi.make_mixer_inputs(100 + l)
             layers.append(dict(qkv=bf(m.qkv), conv_w=bf(m.conv_w), g=f32(m.g), beta=f32(m.beta), z=bf(m.z),
                                norm_w=bf(m.norm_w), cu=torch.from_numpy(m.cu).to(dev)))
+            if args.gates:
+                gt = gi.make_gate_inputs(200 + l, T, Hv)
+                layers[-1].update(a=bf(gt.a), b=bf(gt.b), A_log=f32(gt.A_log), dt_bias=f32(gt.dt_bias))
         cu_host = torch.tensor([0, T], dtype=torch.int64)
         ws = torch.empty(gdn.gdn_mixer_fwd_workspace_size(T, N, Hk, Hv), dtype=torch.uint8, device=dev)
         ys = [torch.empty((T, Hv, D), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
@@ -309,9 +318,14 @@ def main():
 
         def step(i):
             for l, L_ in enumerate(layers):
-                gdn.gdn_mixer_fwd(L_["qkv"], L_["conv_w"], L_["g"], L_["beta"], L_["z"], L_["norm_w"], L_["cu"],
-                                  None, y=ys[l], hT=hs[l], workspace=ws, cu_seqlens_host=cu_host,
-                                  fused_norm=args.fused_norm)
+                if args.gates:
+                    gdn.gdn_mixer_fwd_gates(L_["qkv"], L_["conv_w"], L_["a"], L_["b"], L_["A_log"], L_["dt_bias"],
+                                            L_["z"], L_["norm_w"], L_["cu"], None, y=ys[l], hT=hs[l],
+                                            workspace=ws, cu_seqlens_host=cu_host)
+                else:
+                    gdn.gdn_mixer_fwd(L_["qkv"], L_["conv_w"], L_["g"], L_["beta"], L_["z"], L_["norm_w"], L_["cu"],
+                                      None, y=ys[l], hT=hs[l], workspace=ws, cu_seqlens_host=cu_host,
+                                      fused_norm=args.fused_norm)
         tokens_per_step = T * LAYERS
         layers_per_step = LAYERS
 
@@ -381,7 +395,7 @@ def main():
                                "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4)}}
         pb, pf = path_bytes(T, N, Hk, Hv, with_h0), path_flops(T, Hk, Hv)
     else:
-        pb = layers_per_step * (mixer_bytes(T, N, Hk, Hv))
+        pb = layers_per_step * (mixer_bytes(T, N, Hk, Hv, args.gates))
         pf = layers_per_step * (path_flops(T, Hk, Hv) + T * (2 * Hk + Hv) * D * 8)
         roofline = {"bound": "hbm", "kernel": "mixer step (48 layers)", "achieved": round(pb / (ms_per_step * 1e-3) / 1e9, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -446,6 +460,7 @@ def main():
            "rotating_input_sets": R, "layers_per_step": layers_per_step}
     if mixer:
         cfg["norm"] = "fused into the state pass" if args.fused_norm else "separate kernel"
+        cfg["gates"] = "from the projections" if args.gates else "inputs"
     line = {"metric": "GDN prefill tokens/s per layer (Hk16/Hv32,d128) + % MFMA/HBM roofline",
             "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,

@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_last_hip_error"
                     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_indexed",
                     "gdn_chunk_fwd_noalloc", "gdn_chunk_prep",
                     "gdn_state_pass", "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd", "gdn_mixer_fwd_cont",
-                    "gdn_mixer_fwd_fused_norm")
+                    "gdn_mixer_fwd_fused_norm", "gdn_mixer_fwd_gates")
 
 
 class ChunkDesc(ctypes.Structure):
@@ -98,6 +98,8 @@ def lib():
         L.gdn_mixer_fwd.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11
         L.gdn_mixer_fwd_fused_norm.restype = ctypes.c_int
         L.gdn_mixer_fwd_fused_norm.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11
+        L.gdn_mixer_fwd_gates.restype = ctypes.c_int
+        L.gdn_mixer_fwd_gates.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 13
         L.gdn_mixer_fwd_cont.restype = ctypes.c_int
         L.gdn_mixer_fwd_cont.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 9 + [ctypes.c_int32] + [P] * 5
         _lib_handle = L
@@ -361,6 +363,18 @@ def gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16
     return y, hT
 
 
+def gdn_mixer_fwd_gates(qkv, conv_w, a, b, A_log, dt_bias, z, norm_w, cu_seqlens, h0=None, *, Hk=16, Hv=32,
+                        y=None, hT=None, want_state=True, norm_eps=1e-6, workspace=None, stream=None,
+                        cu_seqlens_host=None):
+    """gdn_mixer_fwd with the gate parameters made in the mixer's first kernel from the projections:
+    g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b) per token and v-head.  a, b: bf16
+    [T, Hv]; A_log, dt_bias: fp32 [Hv].  Returns (y, hT)."""
+    y, hT, _ = _mixer(qkv, conv_w, None, None, z, norm_w, cu_seqlens, h0, None, None, False, Hk, Hv, y, hT, None,
+                      want_state, False, norm_eps, workspace, stream, cu_seqlens_host, False,
+                      gates=(a, b, A_log, dt_bias))
+    return y, hT
+
+
 def gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, conv_in=None, state_index=None, *,
                        Hk=16, Hv=32, y=None, hT=None, conv_out=None, want_state=True, want_window=True,
                        norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
@@ -374,14 +388,21 @@ def gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, con
 
 
 def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, cont, Hk, Hv, y, hT, conv_out,
-           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host, fused_norm=False):
+           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host, fused_norm=False, gates=None):
     dev = qkv.device
     T = int(qkv.shape[0])
     C = (2 * Hk + Hv) * D
     _check(qkv, "qkv", torch.bfloat16, (T, C), dev)
     _check(conv_w, "conv_w", torch.bfloat16, (C, 4), dev)
-    _check(g, "g", torch.float32, (T, Hv), dev)
-    _check(beta, "beta", torch.float32, (T, Hv), dev)
+    if gates is None:
+        _check(g, "g", torch.float32, (T, Hv), dev)
+        _check(beta, "beta", torch.float32, (T, Hv), dev)
+    else:
+        ga, gb, A_log, dt_bias = gates
+        _check(ga, "a", torch.bfloat16, (T, Hv), dev)
+        _check(gb, "b", torch.bfloat16, (T, Hv), dev)
+        _check(A_log, "A_log", torch.float32, (Hv,), dev)
+        _check(dt_bias, "dt_bias", torch.float32, (Hv,), dev)
     _check(z, "z", torch.bfloat16, (T, Hv, D), dev)
     _check(norm_w, "norm_w", torch.bfloat16, (D,), dev)
     N = _check_cu(cu_seqlens, T, cu_seqlens_host)
@@ -422,6 +443,11 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
                                       _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(conv_in), S, _ptr(state_index),
                                       _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream, dev))
         where = "gdn_mixer_fwd_cont"
+    elif gates is not None:
+        rc = lib().gdn_mixer_fwd_gates(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(ga), _ptr(gb), _ptr(A_log),
+                                       _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(y),
+                                       _ptr(hT), _stream(stream, dev))
+        where = "gdn_mixer_fwd_gates"
     else:
         fn, where = ((lib().gdn_mixer_fwd_fused_norm, "gdn_mixer_fwd_fused_norm") if fused_norm
                      else (lib().gdn_mixer_fwd, "gdn_mixer_fwd"))

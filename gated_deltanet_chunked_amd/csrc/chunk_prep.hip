@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec,
-    ConvArgs ca, uint32_t *__restrict__ norm_part) {
+    ConvArgs ca, GateArgs ga, uint32_t *__restrict__ norm_part) {
   static_assert(!kConv || HP == 2, "the input prep runs on pairs of v-heads");
   constexpr int kThreads = 64 * kWavesPerHead * HP, kWaves = kWavesPerHead * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kConv ? kLdsBytes : kOffW];
@@ -288,7 +288,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     }
   }
   const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
-  const float g_raw = g[gi], b_raw = beta[gi];
+  float g_raw, b_raw;
+  if (ga.a) gate_values(ga, gi, h, g_raw, b_raw);  // the gate parameters from the projections
+  else {
+    g_raw = g[gi];
+    b_raw = beta[gi];
+  }
   const float gv = l < L ? g_raw : 0.f;
   const float bv = l < L ? b_raw : 0.f;
   const float G = wave_inclusive_scan(gv);
@@ -523,28 +528,29 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
 }
 
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
-                       const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, uint32_t *norm_part, hipStream_t stream) {
+                       const GateArgs *gates, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
+                       int64_t nslots, void *rec, uint32_t *norm_part, hipStream_t stream) {
+  const GateArgs ga = gates ? *gates : GateArgs{};
   const unsigned short *qp = static_cast<const unsigned short *>(q);
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
   if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
     hipLaunchKernelGGL((chunk_prep_kernel<2, false>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
                        dim3(128 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
-                       ConvArgs{}, norm_part);
+                       ConvArgs{}, ga, norm_part);
   else
     hipLaunchKernelGGL((chunk_prep_kernel<1, false>), dim3((unsigned)nslots, (unsigned)Hv),
                        dim3(64 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
-                       ConvArgs{}, norm_part);
+                       ConvArgs{}, ga, norm_part);
 }
 
 // The same with q, k, v made from the packed mixer input (Hv / Hk even): writes q, k, v (q/k
 // [T, Hk, 128], v [T, Hv, 128], bf16) as the mixer's input prep does, and the records.
 void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
                             const int32_t *state_index, int num_states, const float *g,
-                            const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
-                            int64_t nslots, void *rec, void *qo, void *ko, void *vo,
-                            uint32_t *norm_part, hipStream_t stream) {
+                            const float *beta, const GateArgs *gates, const int32_t *cu, int64_t T,
+                            int N, int Hk, int Hv, int64_t nslots, void *rec, void *qo, void *ko,
+                            void *vo, uint32_t *norm_part, hipStream_t stream) {
   const ConvArgs ca{static_cast<const unsigned short *>(qkv), static_cast<const unsigned short *>(conv_w),
                     static_cast<const unsigned short *>(conv_in), state_index, num_states,
                     static_cast<unsigned short *>(qo), static_cast<unsigned short *>(ko),
@@ -552,7 +558,7 @@ void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *con
   hipLaunchKernelGGL((chunk_prep_kernel<2, true>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
                      dim3(128 * kWavesPerHead), 0, stream, (const unsigned short *)nullptr,
                      (const unsigned short *)nullptr, g, beta, cu, (int)T, N, Hk, Hv,
-                     static_cast<uint8_t *>(rec), ca, norm_part);
+                     static_cast<uint8_t *>(rec), ca, gates ? *gates : GateArgs{}, norm_part);
 }
 
 }  // namespace gdn

@@ -12,8 +12,8 @@
 
 namespace gdn {
 void launch_chunk_prep(const void *q, const void *k, const float *g, const float *beta,
-                       const int32_t *cu, int64_t T, int N, int Hk, int Hv, int64_t nslots,
-                       void *rec, uint32_t *norm_part, hipStream_t stream);
+                       const GateArgs *gates, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
+                       int64_t nslots, void *rec, uint32_t *norm_part, hipStream_t stream);
 hipError_t launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                              const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                              const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
@@ -22,9 +22,9 @@ void launch_state_scan(const float *phi, const float *bend, const float *h0, con
                        int num_h0, float *hs, int segs, int Hv, hipStream_t stream);
 void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
                             const int32_t *state_index, int num_states, const float *g,
-                            const float *beta, const int32_t *cu, int64_t T, int N, int Hk, int Hv,
-                            int64_t nslots, void *rec, void *qo, void *ko, void *vo,
-                            uint32_t *norm_part, hipStream_t stream);
+                            const float *beta, const GateArgs *gates, const int32_t *cu, int64_t T,
+                            int N, int Hk, int Hv, int64_t nslots, void *rec, void *qo, void *ko,
+                            void *vo, uint32_t *norm_part, hipStream_t stream);
 void launch_mixer_prep(const void *qkv, const void *conv_w, const int32_t *cu, int64_t T, int N,
                        int Hk, int Hv, const void *conv_in, const int32_t *state_index,
                        int num_states, void *q, void *k, void *v, hipStream_t stream);
@@ -208,11 +208,12 @@ gdn::SplitPass plan_split(const Shape &s, int max_groups) {
 // of squares as not yet written.
 int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const void *v,
               const float *g, const float *beta, const int32_t *cu, const StatePool &pool, void *o,
-              float *hT, void *ws, hipStream_t stream, const gdn::NormOut *norm = nullptr) {
+              float *hT, void *ws, hipStream_t stream, const gdn::NormOut *norm = nullptr,
+              const gdn::GateArgs *gates = nullptr) {
   unsigned char *rec = static_cast<unsigned char *>(ws);
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   if ((stage & kPrep) && s.T > 0) {
-    gdn::launch_chunk_prep(q, k, g, beta, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec,
+    gdn::launch_chunk_prep(q, k, g, beta, gates, cu, s.T, s.N, s.Hk, s.Hv, s.nslots, rec,
                            norm ? norm->part : nullptr, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip(e);
@@ -448,8 +449,10 @@ size_t gdn_mixer_fwd_workspace_size(const gdn_mixer_desc *d) {
 namespace {
 // The mixer, with the gated RMSNorm as its own kernel after the state pass (fuse_norm false) or
 // fused into the state pass's output path (true; GDN_ERR_UNSUPPORTED where fused_norm_ok fails).
+// gates: g and beta made from the projections (gdn_mixer_fwd_gates; g and beta are then unused).
 int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
-              const float *beta, const void *z, const void *norm_w, const int32_t *cu_seqlens,
+              const float *beta, const gdn::GateArgs *gates, const void *z, const void *norm_w,
+              const int32_t *cu_seqlens,
               const float *h0, const void *conv_in, int32_t num_states, const int32_t *state_index,
               void *y, float *hT, void *conv_out, void *stream, bool fuse_norm_requested) {
   MixerLayout m;
@@ -458,7 +461,10 @@ int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, cons
   const Shape &s = m.s;
   const bool tok = s.T > 0;
   if (!cu_seqlens) return GDN_ERR_NULL;
-  if (tok && (!qkv || !conv_w || !g || !beta || !z || !norm_w || !y)) return GDN_ERR_NULL;
+  if (tok && (!qkv || !conv_w || !z || !norm_w || !y)) return GDN_ERR_NULL;
+  if (tok && !gates && (!g || !beta)) return GDN_ERR_NULL;
+  if (tok && gates && (!gates->a || !gates->b || !gates->A_log || !gates->dt_bias)) return GDN_ERR_NULL;
+  const gdn::GateArgs ga = gates ? *gates : gdn::GateArgs{};
   if (num_states < 1 || (!state_index && num_states != s.N)) return GDN_ERR_SHAPE;
   void *ws = d->chunk.workspace;
   if (!ws || d->chunk.workspace_bytes < m.total) return GDN_ERR_WORKSPACE;
@@ -474,9 +480,12 @@ int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, cons
   const void *a8[] = {conv_w};
   for (const void *p : a8)
     if (p && !aligned(p, 8)) return GDN_ERR_ALIGN;
-  const void *a4[] = {g, beta, cu_seqlens, state_index};
+  const void *a4[] = {g, beta, cu_seqlens, state_index, ga.A_log, ga.dt_bias};
   for (const void *p : a4)
     if (p && !aligned(p, 4)) return GDN_ERR_ALIGN;
+  const void *a2[] = {ga.a, ga.b};
+  for (const void *p : a2)
+    if (p && !aligned(p, 2)) return GDN_ERR_ALIGN;
 
   // In place (hT == h0, conv_out == conv_in) only when sequence n continues from state n.
   const Range outs[] = {{y, tok ? z_b : 0}, {hT, s.N * row_b}, {conv_out, s.N * win_b},
@@ -485,7 +494,9 @@ int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, cons
                        {g, gb_b},          {beta, gb_b},
                        {z, z_b},           {norm_w, nw_b},
                        {cu_seqlens, cu_b}, {h0, (size_t)num_states * row_b},
-                       {conv_in, (size_t)num_states * win_b}, {state_index, (size_t)s.N * 4}};
+                       {conv_in, (size_t)num_states * win_b}, {state_index, (size_t)s.N * 4},
+                       {ga.a, (size_t)s.T * s.Hv * 2},     {ga.b, (size_t)s.T * s.Hv * 2},
+                       {ga.A_log, (size_t)s.Hv * 4},       {ga.dt_bias, (size_t)s.Hv * 4}};
   const InPlace ok[] = {{state_index ? nullptr : hT, h0}, {state_index ? nullptr : conv_out, conv_in}};
   st = check_alias(outs, ins, ok);
   if (st != GDN_OK) return st;
@@ -506,7 +517,7 @@ int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, cons
   // instead of the input prep, then the chunk prep); otherwise the input prep runs first.
   const bool fused = tok && (s.Hv / s.Hk) % 2 == 0;
   if (fused) {
-    gdn::launch_chunk_prep_conv(qkv, conv_w, conv_in, state_index, num_states, g, beta, cu_seqlens,
+    gdn::launch_chunk_prep_conv(qkv, conv_w, conv_in, state_index, num_states, g, beta, gates, cu_seqlens,
                                 s.T, s.N, s.Hk, s.Hv, s.nslots, base, qp, kp, vp,
                                 fuse_norm ? part : nullptr, strm);
     hipError_t e = hipGetLastError();
@@ -526,7 +537,7 @@ int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, cons
   }
   const StatePool pool{h0, num_states, state_index};
   st = run_chunk(s, fused ? kPass : kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm,
-                 fuse_norm ? &norm : nullptr);
+                 fuse_norm ? &norm : nullptr, gates);
   if (st != GDN_OK) return st;
   if (tok && !fuse_norm) {
     gdn::launch_gated_rmsnorm(op, z, norm_w, d->norm_eps, s.T, s.Hv, y, strm);
@@ -544,16 +555,16 @@ int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, const void *con
                        const int32_t *cu_seqlens, const float *h0, const void *conv_in,
                        int32_t num_states, const int32_t *state_index, void *y, float *hT,
                        void *conv_out, void *stream) {
-  return run_mixer(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, num_states, state_index, y,
-                   hT, conv_out, stream, false);
+  return run_mixer(d, qkv, conv_w, g, beta, nullptr, z, norm_w, cu_seqlens, h0, conv_in, num_states,
+                   state_index, y, hT, conv_out, stream, false);
 }
 
 int gdn_mixer_fwd(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const float *g,
                   const float *beta, const void *z, const void *norm_w,
                   const int32_t *cu_seqlens, const float *h0, void *y, float *hT, void *stream) {
   if (!d) return GDN_ERR_NULL;
-  return run_mixer(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, nullptr, d->chunk.num_seqs, nullptr,
-                   y, hT, nullptr, stream, false);
+  return run_mixer(d, qkv, conv_w, g, beta, nullptr, z, norm_w, cu_seqlens, h0, nullptr, d->chunk.num_seqs,
+                   nullptr, y, hT, nullptr, stream, false);
 }
 
 int gdn_mixer_fwd_fused_norm(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
@@ -561,8 +572,19 @@ int gdn_mixer_fwd_fused_norm(const gdn_mixer_desc *d, const void *qkv, const voi
                              const int32_t *cu_seqlens, const float *h0, void *y, float *hT,
                              void *stream) {
   if (!d) return GDN_ERR_NULL;
-  return run_mixer(d, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, nullptr, d->chunk.num_seqs, nullptr,
-                   y, hT, nullptr, stream, true);
+  return run_mixer(d, qkv, conv_w, g, beta, nullptr, z, norm_w, cu_seqlens, h0, nullptr, d->chunk.num_seqs,
+                   nullptr, y, hT, nullptr, stream, true);
+}
+
+int gdn_mixer_fwd_gates(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const void *a,
+                        const void *b, const float *A_log, const float *dt_bias, const void *z,
+                        const void *norm_w, const int32_t *cu_seqlens, const float *h0, void *y,
+                        float *hT, void *stream) {
+  if (!d) return GDN_ERR_NULL;
+  const gdn::GateArgs ga{static_cast<const unsigned short *>(a), static_cast<const unsigned short *>(b),
+                         A_log, dt_bias};
+  return run_mixer(d, qkv, conv_w, nullptr, nullptr, &ga, z, norm_w, cu_seqlens, h0, nullptr,
+                   d->chunk.num_seqs, nullptr, y, hT, nullptr, stream, false);
 }
 
 }  // extern "C"

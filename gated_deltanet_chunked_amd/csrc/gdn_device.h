@@ -144,6 +144,24 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// Gate parameters made from the layer's projections (gdn_mixer_fwd_gates): for token t and v-head
+// h, g = -exp(A_log[h]) softplus(a[t,h] + dt_bias[h]) and beta = sigmoid(b[t,h]), with a, b bf16
+// [T, Hv] and A_log, dt_bias fp32 [Hv].  With a null the kernels read g and beta as given.
+struct GateArgs {
+  const unsigned short *a, *b;
+  const float *A_log, *dt_bias;
+};
+// On the hardware exp2, log2 and reciprocal (about 1 ulp each): softplus(x) = max(x, 0) +
+// ln 2 log2(1 + 2^(-|x| log2 e)) never overflows, and its absolute error stays near 1e-7 where the
+// log2 argument rounds to 1 (|x| > 17, softplus below 4e-8), far inside what the decay needs.
+__device__ __forceinline__ void gate_values(const GateArgs &ga, size_t i, int h, float &g, float &beta) {
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  const float x = bits_to_float(ga.a[i]) + ga.dt_bias[h];
+  const float sp = fmaxf(x, 0.f) + kLn2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e));
+  g = -__builtin_amdgcn_exp2f(ga.A_log[h] * kLog2e) * sp;
+  beta = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-bits_to_float(ga.b[i]) * kLog2e));
+}
+
 // Carried conv window of sequence n ([W, C] bf16, oldest row first), or null for zeros.
 __device__ __forceinline__ const unsigned short *window_of(const unsigned short *conv_in,
                                                            const int32_t *state_index,

@@ -171,6 +171,27 @@ def make_mixer_inputs(seed: int, lengths=(MIXER_T,), Hk: int = 16, Hv: int = 32,
     return MixerInputs(qkv, conv_w, beta, g, z, norm_w, cu, h0)
 
 
+@dataclass
+class GateInputs:
+    a: np.ndarray        # uint16 bf16 bits [T, Hv]: the projection row that sets the decay
+    b: np.ndarray        # uint16 bf16 bits [T, Hv]: the projection row that sets beta
+    A_log: np.ndarray    # float32 [Hv]
+    dt_bias: np.ndarray  # float32 [Hv]
+
+
+def make_gate_inputs(seed: int, T: int, Hv: int) -> GateInputs:
+    """Inputs of the gate-parameter step: a, b ~ N(0, 1) in bf16; per head A_log = log A with
+    A ~ U(1, 16) and dt_bias = log(expm1(dt)) with log dt ~ U(log 1e-3, log 1e-1), the customary
+    initialisation of a Mamba2-style gate (softplus(dt_bias) = dt)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = bf16_bits(rng.standard_normal((T, Hv)))
+    b = bf16_bits(rng.standard_normal((T, Hv)))
+    A_log = np.log(rng.uniform(1.0, 16.0, Hv)).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), Hv))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    return GateInputs(a, b, A_log, dt_bias)
+
+
 # ----------------------------------------------------------------------------------------------
 # Carried states for continuation: pools of initial recurrent states and conv input windows.
 # ----------------------------------------------------------------------------------------------

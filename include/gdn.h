@@ -238,6 +238,26 @@ GDN_EXPORT int gdn_mixer_fwd_fused_norm(const gdn_mixer_desc *d, const void *qkv
                                         const float *h0, void *y, float *hT, void *stream);
 
 /*
+ * gdn_mixer_fwd with the gate parameters made inside the mixer's first kernel from the layer's
+ * projections, in place of g and beta as inputs (the "open-jev-fast" README, "Phase 2" item 1,
+ * lists "gate parameters" as the last step of its fused GDN input prep).  The pages give no
+ * formula; this follows the Mamba2-style gating of the Gated DeltaNet paper that README cites
+ * (Yang, Kautz & Hatamizadeh, ICLR 2025): for token t and v-head h,
+ *     g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])     (log-decay, < 0)
+ *     beta[t,h] = sigmoid(b[t,h])
+ * computed in fp32 (expf / log1pf; softplus without overflow).
+ *   a, b          : bf16 [T, Hv] (2-byte aligned) -- the projections' gate rows
+ *   A_log, dt_bias: fp32 [Hv] (4-byte aligned)    -- per-head parameters
+ * Every other argument, the workspace (gdn_mixer_fwd_workspace_size) and the errors are
+ * gdn_mixer_fwd's; a, b, A_log and dt_bias may be NULL only when T == 0.  Inputs are only read.
+ */
+GDN_EXPORT int gdn_mixer_fwd_gates(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                                   const void *a, const void *b, const float *A_log,
+                                   const float *dt_bias, const void *z, const void *norm_w,
+                                   const int32_t *cu_seqlens, const float *h0, void *y, float *hT,
+                                   void *stream);
+
+/*
  * The mixer continuing from carried states: beside the recurrent state, each sequence carries
  * the conv input window -- the last conv_taps - 1 rows of qkv before it -- so that both can pass
  * from a prefix to the candidates that continue it (the "open-jev-fast" README, "Phase 2" item 2,

@@ -179,6 +179,37 @@ def test_mixer_validation(entry):
     assert call(big) == gdn.GDN_ERR_SHAPE
 
 
+def test_mixer_gates_validation():
+    # the gates entry point: gdn_mixer_fwd's checks, with a, b (bf16 [T, Hv]) and A_log, dt_bias
+    # (fp32 [Hv]) in place of g and beta; every check runs before anything is launched
+    a = _addrs()
+    ws = gdn.gdn_mixer_fwd_workspace_size(T, N, HK, HV)
+    P = ctypes.c_void_p
+    fn = gdn.lib().gdn_mixer_fwd_gates
+
+    def call(m, **over):
+        b = {"qkv": a["q"], "cw": a["k"], "ga": a["g"], "gb": a["beta"], "A_log": a["cu"] + GB // 2,
+             "dt": a["cu"] + GB // 2 + 256, "z": a["v"], "nw": a["h0"] + GB // 2, "cu": a["cu"], "h0": a["h0"],
+             "y": a["o"], "hT": a["hT"]}
+        b.update(over)
+        pp = lambda x: None if x is None else P(x)
+        return fn(ctypes.byref(m) if m is not None else None, pp(b["qkv"]), pp(b["cw"]), pp(b["ga"]), pp(b["gb"]),
+                  pp(b["A_log"]), pp(b["dt"]), pp(b["z"]), pp(b["nw"]), pp(b["cu"]), pp(b["h0"]), pp(b["y"]),
+                  pp(b["hT"]), None)
+
+    good = lambda wsb=ws: gdn.MixerDesc(gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], wsb), 4, 1e-6)
+    assert call(None) == gdn.GDN_ERR_NULL
+    for field in ("ga", "gb", "A_log", "dt"):
+        assert call(good(), **{field: None}) == gdn.GDN_ERR_NULL, field
+    assert call(good(wsb=ws - 1)) == gdn.GDN_ERR_WORKSPACE
+    assert call(good(), ga=a["g"] + 1) == gdn.GDN_ERR_ALIGN
+    assert call(good(), gb=a["beta"] + 1) == gdn.GDN_ERR_ALIGN
+    assert call(good(), A_log=a["cu"] + GB // 2 + 2) == gdn.GDN_ERR_ALIGN
+    assert call(good(), dt=a["cu"] + GB // 2 + 258) == gdn.GDN_ERR_ALIGN
+    assert call(good(), y=a["g"]) == gdn.GDN_ERR_ALIAS          # y over a
+    assert call(good(), hT=a["cu"] + GB // 2) == gdn.GDN_ERR_ALIAS  # hT over A_log
+
+
 def _call_indexed(num_h0=3, idx=None, **over):
     a = _addrs()
     a["idx"] = a["cu"] + GB // 2

@@ -1,6 +1,8 @@
 """gdn_mixer_fwd (HIP) against the fp64 mixer oracle: y rel-L2 <= 5e-3, an elementwise bound on y
 propagated from the 2e-2 max-abs tolerance of o through the gated RMSNorm (see check_mixer), and
 hT rel-L2 <= 1e-3."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -140,3 +142,33 @@ def test_mixer_head_ratios(Hk, Hv):
     say(f"[mixer] head ratio Hk={Hk} Hv={Hv} lengths={lengths} with h0")
     m = gi.make_mixer_inputs(300 + 10 * Hk + Hv, lengths=lengths, Hk=Hk, Hv=Hv, with_h0=True)
     check_mixer(*run_mixer_gpu(m, Hk, Hv), *run_mixer_oracle(m, Hk, Hv), f"Hk={Hk} Hv={Hv}", m)
+
+
+@pytest.mark.parametrize("case", ["t936", "varlen_ratio1", "varlen_ratio3"])
+def test_mixer_gates(case):
+    # gdn_mixer_fwd_gates: g = -exp(A_log) softplus(a + dt_bias) and beta = sigmoid(b) made in the
+    # mixer's first kernel (fp32 on the GPU), against the oracle's gates (fp64) fed to the mixer
+    # oracle.  Ratio 2 runs them in the chunk prep that also makes q, k, v; ratios 1 and 3 in the
+    # chunk prep after the separate input prep.
+    if case == "t936":
+        m, Hk, Hv = gi.make_mixer_inputs(100), 16, 32
+    elif case == "varlen_ratio1":
+        m, Hk, Hv = gi.make_mixer_inputs(11, lengths=[70, 1, 200, 33], Hk=2, Hv=2, with_h0=True), 2, 2
+    else:
+        m, Hk, Hv = gi.make_mixer_inputs(12, lengths=[129, 64, 5], Hk=1, Hv=3), 1, 3
+    T = m.qkv.shape[0]
+    gt = gi.make_gate_inputs(200, T, Hv)
+    say(f"[mixer-gates] {case} Hk={Hk} Hv={Hv} T={T}")
+    f = gi.bits_to_f64
+    g, beta = oracle.gates(f(gt.a), f(gt.b), gt.A_log.astype(np.float64), gt.dt_bias.astype(np.float64))
+    say(f"  g in [{g.min():.3f}, {g.max():.3f}], beta in [{beta.min():.3f}, {beta.max():.3f}]")
+    y, hT = gdn.gdn_mixer_fwd_gates(bf16_dev(m.qkv), bf16_dev(m.conv_w), bf16_dev(gt.a), bf16_dev(gt.b),
+                                    f32_dev(gt.A_log), f32_dev(gt.dt_bias), bf16_dev(m.z), bf16_dev(m.norm_w),
+                                    torch.from_numpy(m.cu.astype(np.int32)).cuda(),
+                                    None if m.h0 is None else f32_dev(m.h0), Hk=Hk, Hv=Hv,
+                                    cu_seqlens_host=torch.from_numpy(m.cu.astype(np.int64)))
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    hT = hT.cpu().numpy().astype(np.float64)
+    mg = dataclasses.replace(m, g=g, beta=beta)
+    check_mixer(y, hT, *run_mixer_oracle(mg, Hk, Hv), f"gates {case}", mg)
