@@ -297,8 +297,11 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
   const float gv = l < L ? g_raw : 0.f;
   const float bv = l < L ? b_raw : 0.f;
   const float G = wave_inclusive_scan(gv);
-  const float Glast = __shfl(G, 63, 64);
-  const float Gref = __shfl(G, wl == 0 ? (l & ~15) : 16 * (wl & 3), 64);
+  const float Glast = lane_value(G, 63);
+  // wave 0 of a head: G at the first token of this lane's 16-row block; waves 1-3: G at 16 wl
+  const float Gref = wl == 0 ? ((l >> 4) == 0 ? lane_value(G, 0) : (l >> 4) == 1 ? lane_value(G, 16)
+                                : (l >> 4) == 2 ? lane_value(G, 32) : lane_value(G, 48))
+                             : lane_value(G, 16 * (wl & 3));
   if (wl == 0) {
     Gall[kChunk * hh + l] = G;
     Ball[kChunk * hh + l] = bv;

@@ -114,15 +114,27 @@ __device__ __forceinline__ void store_bf16x8(void *p, bf16x8 x) {
   *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, x);
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// x of another lane through a DPP lane pattern (a vector ALU operand modifier, no LDS round trip);
+// lanes that the pattern gives no source, or that RowMask leaves out, read 0.
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, RowMask, 0xf, true));
+}
+// Inclusive prefix sum across the 64 lanes of a wave, on DPP: a Hillis-Steele scan inside each
+// 16-lane row (row_shr 1, 2, 4, 8), then each row's total carried into the rows after it
+// (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3; gfx9 DPP).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x += dpp_or_zero<0x111>(x);
+  x += dpp_or_zero<0x112>(x);
+  x += dpp_or_zero<0x114>(x);
+  x += dpp_or_zero<0x118>(x);
+  x += dpp_or_zero<0x142, 0xa>(x);
+  x += dpp_or_zero<0x143, 0xc>(x);
   return x;
+}
+// x of lane `lane` (wave-uniform) in every lane.
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 // ---- GDN mixer input prep (conv + SiLU + L2 norm): shared by mixer_prep_kernel and the prep
@@ -138,9 +150,12 @@ __device__ __forceinline__ float silu(float x) {
 __device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
 
 __device__ __forceinline__ float sum16(float x) {
-  // butterfly over the 16 lanes that share l / 16
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+  // sum over the 16 lanes that share l / 16, on DPP: rotations by 8 and 4 inside the row, then
+  // the quad permutations [1,0,3,2] and [2,3,0,1]; every lane ends with the row's sum
+  x += dpp_or_zero<0x128>(x);
+  x += dpp_or_zero<0x124>(x);
+  x += dpp_or_zero<0xB1>(x);
+  x += dpp_or_zero<0x4E>(x);
   return x;
 }
 
