@@ -129,7 +129,8 @@ struct ConvArgs {
 // T' fragments spread over all of them; the diagonal solve and the column chains run on the first
 // 4 waves of each head.
 constexpr int kWavesPerHead = 8;
-template <int HP, bool kConv>
+// kGates: g and beta made from the projections (ga), else read as given.
+template <int HP, bool kConv, bool kGates>
 __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -287,9 +288,13 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
       *reinterpret_cast<u32x4 *>(Qs + so) = row < L ? qv[it] : zero;
     }
   }
+  // The gates are loaded once the q/k data has arrived (the scheduling barrier keeps the compiler
+  // from hoisting them): issued together with the q/k loads, these small loads -- one 128-byte line
+  // per lane -- measured slower (prep 78.5 -> 82.3 us at T = 16,384).
+  __builtin_amdgcn_sched_barrier(0);
   const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
   float g_raw, b_raw;
-  if (ga.a) gate_values(ga, gi, h, g_raw, b_raw);  // the gate parameters from the projections
+  if constexpr (kGates) gate_values(gate_load(ga, gi, h), g_raw, b_raw);  // from the projections
   else {
     g_raw = g[gi];
     b_raw = beta[gi];
@@ -537,14 +542,22 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
   const unsigned short *qp = static_cast<const unsigned short *>(q);
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
-  if ((Hv / Hk) % 2 == 0)  // pairs of v-heads of one k-head per workgroup
-    hipLaunchKernelGGL((chunk_prep_kernel<2, false>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
-                       dim3(128 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
-                       ConvArgs{}, ga, norm_part);
-  else
-    hipLaunchKernelGGL((chunk_prep_kernel<1, false>), dim3((unsigned)nslots, (unsigned)Hv),
-                       dim3(64 * kWavesPerHead), 0, stream, qp, kp, g, beta, cu, (int)T, N, Hk, Hv, rp,
-                       ConvArgs{}, ga, norm_part);
+  const dim3 pairs((unsigned)nslots, (unsigned)(Hv / 2)), singles((unsigned)nslots, (unsigned)Hv);
+  if ((Hv / Hk) % 2 == 0) {  // pairs of v-heads of one k-head per workgroup
+    if (gates)
+      hipLaunchKernelGGL((chunk_prep_kernel<2, false, true>), pairs, dim3(128 * kWavesPerHead), 0, stream, qp,
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<2, false, false>), pairs, dim3(128 * kWavesPerHead), 0, stream, qp,
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+  } else {
+    if (gates)
+      hipLaunchKernelGGL((chunk_prep_kernel<1, false, true>), singles, dim3(64 * kWavesPerHead), 0, stream, qp,
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<1, false, false>), singles, dim3(64 * kWavesPerHead), 0, stream, qp,
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+  }
 }
 
 // The same with q, k, v made from the packed mixer input (Hv / Hk even): writes q, k, v (q/k
@@ -558,10 +571,14 @@ void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *con
                     static_cast<const unsigned short *>(conv_in), state_index, num_states,
                     static_cast<unsigned short *>(qo), static_cast<unsigned short *>(ko),
                     static_cast<unsigned short *>(vo)};
-  hipLaunchKernelGGL((chunk_prep_kernel<2, true>), dim3((unsigned)nslots, (unsigned)(Hv / 2)),
-                     dim3(128 * kWavesPerHead), 0, stream, (const unsigned short *)nullptr,
-                     (const unsigned short *)nullptr, g, beta, cu, (int)T, N, Hk, Hv,
-                     static_cast<uint8_t *>(rec), ca, gates ? *gates : GateArgs{}, norm_part);
+  const dim3 grid((unsigned)nslots, (unsigned)(Hv / 2));
+  const unsigned short *none = nullptr;
+  if (gates)
+    hipLaunchKernelGGL((chunk_prep_kernel<2, true, true>), grid, dim3(128 * kWavesPerHead), 0, stream, none,
+                       none, g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec), ca, *gates, norm_part);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<2, true, false>), grid, dim3(128 * kWavesPerHead), 0, stream, none,
+                       none, g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec), ca, GateArgs{}, norm_part);
 }
 
 }  // namespace gdn

@@ -166,15 +166,24 @@ struct GateArgs {
   const unsigned short *a, *b;
   const float *A_log, *dt_bias;
 };
+// The inputs of one (token i, v-head h), loaded apart from the arithmetic so that the loads can be
+// issued with the kernel's other loads.
+struct GateIn {
+  unsigned short a, b;
+  float A_log, dt_bias;
+};
+__device__ __forceinline__ GateIn gate_load(const GateArgs &ga, size_t i, int h) {
+  return GateIn{ga.a[i], ga.b[i], ga.A_log[h], ga.dt_bias[h]};
+}
 // On the hardware exp2, log2 and reciprocal (about 1 ulp each): softplus(x) = max(x, 0) +
 // ln 2 log2(1 + 2^(-|x| log2 e)) never overflows, and its absolute error stays near 1e-7 where the
 // log2 argument rounds to 1 (|x| > 17, softplus below 4e-8), far inside what the decay needs.
-__device__ __forceinline__ void gate_values(const GateArgs &ga, size_t i, int h, float &g, float &beta) {
+__device__ __forceinline__ void gate_values(const GateIn &in, float &g, float &beta) {
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
-  const float x = bits_to_float(ga.a[i]) + ga.dt_bias[h];
+  const float x = bits_to_float(in.a) + in.dt_bias;
   const float sp = fmaxf(x, 0.f) + kLn2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e));
-  g = -__builtin_amdgcn_exp2f(ga.A_log[h] * kLog2e) * sp;
-  beta = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-bits_to_float(ga.b[i]) * kLog2e));
+  g = -__builtin_amdgcn_exp2f(in.A_log * kLog2e) * sp;
+  beta = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-bits_to_float(in.b) * kLog2e));
 }
 
 // Carried conv window of sequence n ([W, C] bf16, oldest row first), or null for zeros.
