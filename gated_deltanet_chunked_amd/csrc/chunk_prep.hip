@@ -290,32 +290,34 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
   }
   // The gates are loaded once the q/k data has arrived (the scheduling barrier keeps the compiler
   // from hoisting them): issued together with the q/k loads, these small loads -- one 128-byte line
-  // per lane -- measured slower (prep 78.5 -> 82.3 us at T = 16,384).
+  // per lane -- measured slower (prep 78.5 -> 82.3 us at T = 16,384).  One wave per v-head loads
+  // them and makes the cumsum, the decay tables and the record's decays.
   __builtin_amdgcn_sched_barrier(0);
-  const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
-  float g_raw, b_raw;
-  if constexpr (kGates) gate_values(gate_load(ga, gi, h), g_raw, b_raw);  // from the projections
-  else {
-    g_raw = g[gi];
-    b_raw = beta[gi];
-  }
-  const float gv = l < L ? g_raw : 0.f;
-  const float bv = l < L ? b_raw : 0.f;
-  const float G = wave_inclusive_scan(gv);
-  const float Glast = lane_value(G, 63);
-  // wave 0 of a head: G at the first token of this lane's 16-row block; waves 1-3: G at 16 wl
-  const float Gref = wl == 0 ? ((l >> 4) == 0 ? lane_value(G, 0) : (l >> 4) == 1 ? lane_value(G, 16)
-                                : (l >> 4) == 2 ? lane_value(G, 32) : lane_value(G, 48))
-                             : lane_value(G, 16 * (wl & 3));
   if (wl == 0) {
+    const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
+    float g_raw, b_raw;
+    if constexpr (kGates) gate_values(gate_load(ga, gi, h), g_raw, b_raw);  // from the projections
+    else {
+      g_raw = g[gi];
+      b_raw = beta[gi];
+    }
+    const float gv = l < L ? g_raw : 0.f;
+    const float bv = l < L ? b_raw : 0.f;
+    const float G = wave_inclusive_scan(gv);
+    const float Glast = lane_value(G, 63);
+    const float G16 = lane_value(G, 16), G32 = lane_value(G, 32), G48 = lane_value(G, 48);
+    // Er: G relative to the first token of this lane's 16-row block
+    const float Gr = (l >> 4) == 0 ? lane_value(G, 0) : (l >> 4) == 1 ? G16 : (l >> 4) == 2 ? G32 : G48;
     Gall[kChunk * hh + l] = G;
     Ball[kChunk * hh + l] = bv;
-    Erall[kChunk * hh + l] = exp_neg(G - Gref);
+    Erall[kChunk * hh + l] = exp_neg(G - Gr);
+    // Fc[rb - 1][j] = e^{G_{16 rb} - G_j} for j < 16 rb
+    Fcall[kChunk * (3 * hh + 0) + l] = l < 16 ? exp_neg(G16 - G) : 0.f;
+    Fcall[kChunk * (3 * hh + 1) + l] = l < 32 ? exp_neg(G32 - G) : 0.f;
+    Fcall[kChunk * (3 * hh + 2) + l] = l < 48 ? exp_neg(G48 - G) : 0.f;
     uint8_t *R = rec_slot + (size_t)h * kRecBytes;
     __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
     __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
-  } else if (wl < 4) {
-    Fcall[kChunk * (3 * hh + wl - 1) + l] = l < 16 * wl ? exp_neg(Gref - G) : 0.f;
   }
   __syncthreads();
 
