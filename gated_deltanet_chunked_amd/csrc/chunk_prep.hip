@@ -290,34 +290,43 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
   }
   // The gates are loaded once the q/k data has arrived (the scheduling barrier keeps the compiler
   // from hoisting them): issued together with the q/k loads, these small loads -- one 128-byte line
-  // per lane -- measured slower (prep 78.5 -> 82.3 us at T = 16,384).  One wave per v-head loads
-  // them and makes the cumsum, the decay tables and the record's decays.
+  // per lane -- measured slower (prep 78.5 -> 82.3 us at T = 16,384).  The first wave loads them
+  // for the workgroup's v-heads at once (adjacent in each row) and makes their cumsums, decay
+  // tables and record decays.
   __builtin_amdgcn_sched_barrier(0);
-  if (wl == 0) {
-    const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h;
-    float g_raw, b_raw;
-    if constexpr (kGates) gate_values(gate_load(ga, gi, h), g_raw, b_raw);  // from the projections
-    else {
-      g_raw = g[gi];
-      b_raw = beta[gi];
+  if (w == 0) {
+    const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h_first;
+    float g_raw[HP], b_raw[HP];
+    if constexpr (kGates) {
+#pragma unroll
+      for (int x = 0; x < HP; ++x) gate_values(gate_load(ga, gi + x, h_first + x), g_raw[x], b_raw[x]);
+    } else if constexpr (HP == 2) {
+      const f32x2 g2 = *reinterpret_cast<const f32x2 *>(g + gi), b2 = *reinterpret_cast<const f32x2 *>(beta + gi);
+      g_raw[0] = g2[0], g_raw[1] = g2[1], b_raw[0] = b2[0], b_raw[1] = b2[1];
+    } else {
+      g_raw[0] = g[gi];
+      b_raw[0] = beta[gi];
     }
-    const float gv = l < L ? g_raw : 0.f;
-    const float bv = l < L ? b_raw : 0.f;
-    const float G = wave_inclusive_scan(gv);
-    const float Glast = lane_value(G, 63);
-    const float G16 = lane_value(G, 16), G32 = lane_value(G, 32), G48 = lane_value(G, 48);
-    // Er: G relative to the first token of this lane's 16-row block
-    const float Gr = (l >> 4) == 0 ? lane_value(G, 0) : (l >> 4) == 1 ? G16 : (l >> 4) == 2 ? G32 : G48;
-    Gall[kChunk * hh + l] = G;
-    Ball[kChunk * hh + l] = bv;
-    Erall[kChunk * hh + l] = exp_neg(G - Gr);
-    // Fc[rb - 1][j] = e^{G_{16 rb} - G_j} for j < 16 rb
-    Fcall[kChunk * (3 * hh + 0) + l] = l < 16 ? exp_neg(G16 - G) : 0.f;
-    Fcall[kChunk * (3 * hh + 1) + l] = l < 32 ? exp_neg(G32 - G) : 0.f;
-    Fcall[kChunk * (3 * hh + 2) + l] = l < 48 ? exp_neg(G48 - G) : 0.f;
-    uint8_t *R = rec_slot + (size_t)h * kRecBytes;
-    __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
-    __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
+#pragma unroll
+    for (int x = 0; x < HP; ++x) {
+      const float gv = l < L ? g_raw[x] : 0.f;
+      const float bv = l < L ? b_raw[x] : 0.f;
+      const float G = wave_inclusive_scan(gv);
+      const float Glast = lane_value(G, 63);
+      const float G16 = lane_value(G, 16), G32 = lane_value(G, 32), G48 = lane_value(G, 48);
+      // Er: G relative to the first token of this lane's 16-row block
+      const float Gr = (l >> 4) == 0 ? lane_value(G, 0) : (l >> 4) == 1 ? G16 : (l >> 4) == 2 ? G32 : G48;
+      Gall[kChunk * x + l] = G;
+      Ball[kChunk * x + l] = bv;
+      Erall[kChunk * x + l] = exp_neg(G - Gr);
+      // Fc[rb - 1][j] = e^{G_{16 rb} - G_j} for j < 16 rb
+      Fcall[kChunk * (3 * x + 0) + l] = l < 16 ? exp_neg(G16 - G) : 0.f;
+      Fcall[kChunk * (3 * x + 1) + l] = l < 32 ? exp_neg(G32 - G) : 0.f;
+      Fcall[kChunk * (3 * x + 2) + l] = l < 48 ? exp_neg(G48 - G) : 0.f;
+      uint8_t *R = rec_slot + (size_t)(h_first + x) * kRecBytes;
+      __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
+      __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
+    }
   }
   __syncthreads();
 
