@@ -182,6 +182,26 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
   static_assert(kThreads == kChunk * HP * kDvTiles, "one word of norm_part per thread");
 
   // ---- 1. global loads up front; gate cumsum per v-head --------------------------------------
+  // The first wave loads the gates (or their inputs) of the workgroup's v-heads -- adjacent in each
+  // row, one load per token for both -- together with its q/k loads (every wave loading its own
+  // head's gates, once the q/k data had arrived, took 79.2 us at T = 16,384 against 66.8), and
+  // later makes their cumsums, decay tables and record decays.
+  const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h_first;
+  float g_raw[HP] = {}, b_raw[HP] = {};
+  GateIn gin[HP] = {};
+  auto load_gates = [&]() {
+    if (w != 0) return;
+    if constexpr (kGates) {
+#pragma unroll
+      for (int x = 0; x < HP; ++x) gin[x] = gate_load(ga, gi + x, h_first + x);
+    } else if constexpr (HP == 2) {
+      const f32x2 g2 = *reinterpret_cast<const f32x2 *>(g + gi), b2 = *reinterpret_cast<const f32x2 *>(beta + gi);
+      g_raw[0] = g2[0], g_raw[1] = g2[1], b_raw[0] = b2[0], b_raw[1] = b2[1];
+    } else {
+      g_raw[0] = g[gi];
+      b_raw[0] = beta[gi];
+    }
+  };
   constexpr int kIt = 1024 / kThreads;  // 16-byte pieces of one 64 x 128 tile per thread
   if constexpr (kConv) {
     // Waves 4 b .. 4 b + 3 make block b of the four 128-channel blocks q, k (k-head hk), v (v-heads
@@ -279,6 +299,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
       kv[it] = *reinterpret_cast<const u32x4 *>(k + off);
       qv[it] = *reinterpret_cast<const u32x4 *>(q + off);
     }
+    load_gates();
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int p = tid + kThreads * it, row = p >> 4, ch = p & 15;
@@ -288,24 +309,15 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
       *reinterpret_cast<u32x4 *>(Qs + so) = row < L ? qv[it] : zero;
     }
   }
-  // The gates are loaded once the q/k data has arrived (the scheduling barrier keeps the compiler
-  // from hoisting them): issued together with the q/k loads, these small loads -- one 128-byte line
-  // per lane -- measured slower (prep 78.5 -> 82.3 us at T = 16,384).  The first wave loads them
-  // for the workgroup's v-heads at once (adjacent in each row) and makes their cumsums, decay
-  // tables and record decays.
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kConv) {
+    // after the input prep (issued with its row loads, the gate loads measured slower)
+    __builtin_amdgcn_sched_barrier(0);
+    load_gates();
+  }
   if (w == 0) {
-    const size_t gi = (size_t)(t0 + min(l, L - 1)) * Hv + h_first;
-    float g_raw[HP], b_raw[HP];
     if constexpr (kGates) {
 #pragma unroll
-      for (int x = 0; x < HP; ++x) gate_values(gate_load(ga, gi + x, h_first + x), g_raw[x], b_raw[x]);
-    } else if constexpr (HP == 2) {
-      const f32x2 g2 = *reinterpret_cast<const f32x2 *>(g + gi), b2 = *reinterpret_cast<const f32x2 *>(beta + gi);
-      g_raw[0] = g2[0], g_raw[1] = g2[1], b_raw[0] = b2[0], b_raw[1] = b2[1];
-    } else {
-      g_raw[0] = g[gi];
-      b_raw[0] = beta[gi];
+      for (int x = 0; x < HP; ++x) gate_values(gin[x], g_raw[x], b_raw[x]);  // from the projections
     }
 #pragma unroll
     for (int x = 0; x < HP; ++x) {
