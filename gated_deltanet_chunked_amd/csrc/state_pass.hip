@@ -1124,7 +1124,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
 
   // Compute waves.  State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].
   // At the last chunk of an item the final state is stored and the next item's initial state,
-  // loaded during that chunk, takes its place before H (hi and lo) goes to LDS.
+  // loaded from the item's first chunk on (items of short sequences last one or two chunks, less
+  // than a load from memory), takes its place before H (hi and lo) goes to LDS.
   Walker cur;
   cur.k = -1;
   next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
@@ -1137,8 +1138,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   read_k_rows(ka, tiles, w, l);
   for (int s = 0; cur.valid; ++s) {
     const bool last = cur.c == cur.it.nc - 1;
-    Walker nx = cur;
-    if (last) {
+    if (cur.c == 0) {
+      Walker nx = cur;
       next_item(nx, gr, cu);  // the next item's initial state (copies of empty items come later)
       if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
     }
