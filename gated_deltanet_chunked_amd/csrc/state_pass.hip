@@ -276,6 +276,7 @@ constexpr int kDecED = kRecED - kRecEG;
 struct PrefetchLane {
   const unsigned char *ptr[2];
   uint32_t adv[2];
+  int row[2];  // the line's token row within a chunk; -1 for record lines (no rows)
 };
 __device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, int hk, int h, int Hk,
                                                        int Hv, int tile, int gi, int ng, int l,
@@ -292,12 +293,14 @@ __device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, in
     int s = 64 * j + l;
     pf.ptr[j] = nullptr;
     pf.adv[j] = 0;
+    pf.row[j] = -1;
     if (s < nkq) {
       const int m = gi + ng * s;
       const unsigned short *base = (m >> 7) ? q : k;
       pf.ptr[j] = reinterpret_cast<const unsigned char *>(
                       base + ((size_t)(tb + ((m >> 1) & 63)) * Hk + hk) * kDim) + 128 * (m & 1);
       pf.adv[j] = (uint32_t)(kChunk * Hk * kDim * 2);
+      pf.row[j] = (m >> 1) & 63;
     } else if ((s -= nkq) < nrec) {
       pf.ptr[j] = rec + ((size_t)slot0 * Hv + h) * kRecBytes + 128 * (tile + 8 * s);
       pf.adv[j] = (uint32_t)(Hv * kRecBytes);
@@ -306,6 +309,7 @@ __device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, in
       pf.ptr[j] = reinterpret_cast<const unsigned char *>(
                       v + ((size_t)(tb + (m >> 1)) * Hv + h) * kDim) + 128 * (m & 1);
       pf.adv[j] = (uint32_t)(kChunk * Hv * kDim * 2);
+      pf.row[j] = m >> 1;
     }
   }
   return pf;
@@ -998,8 +1002,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
 
   if (w == kPrefetchWave) {
     // Prefetch wave: warms L2 kPrefetchAhead steps ahead of use and never waits for its loads
-    // inside the loop (so a slow line holds up nothing).  Barriers as the compute waves.  A
-    // sequence's partial last chunk is not warmed (its rows past the end must not be read).
+    // inside the loop (so a slow line holds up nothing).  Barriers as the compute waves.  Of a
+    // sequence's partial last chunk only the rows that exist are warmed (items of short sequences
+    // are mostly such chunks).
     Walker cur = first_step(gr, cu);
     if (cur.valid) {
       const unsigned sink = (unsigned)(uintptr_t)touch_sink;
@@ -1012,16 +1017,15 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
       for (int s = 0; cur.valid; ++s) {
         for (int cnt = s == 0 ? kPrefetchAhead - 2 : 1; cnt > 0 && pf.valid; --cnt) {
           const Item &it = pf.it;
-          if (pf.c < (it.te - it.tb) / kChunk) {  // full chunk
-            if (pl_k != pf.k) {
-              pl = prefetch_lanes(it.tb, it.slot0, it.hk, it.h, Hk, Hv, tile, tile * r + it.h - it.hk * r,
-                                  kDvTiles * r, l, q, k, v, rec);
-              pl_k = pf.k;
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              if (pl.ptr[j]) touch(pl.ptr[j] + (size_t)pf.c * pl.adv[j], sink);
+          if (pl_k != pf.k) {
+            pl = prefetch_lanes(it.tb, it.slot0, it.hk, it.h, Hk, Hv, tile, tile * r + it.h - it.hk * r,
+                                kDvTiles * r, l, q, k, v, rec);
+            pl_k = pf.k;
           }
+          const int rows = min(kChunk, it.te - it.tb - kChunk * pf.c);  // rows of this chunk
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (pl.ptr[j] && pl.row[j] < rows) touch(pl.ptr[j] + (size_t)pf.c * pl.adv[j], sink);
           next_step(pf, gr, cu);
         }
         dma_barrier();
