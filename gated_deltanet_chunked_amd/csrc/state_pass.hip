@@ -626,6 +626,7 @@ struct Item {
 };
 struct Walker {
   int k, c;  // item round, chunk within the item
+  int ord;   // ordinal of the item among the workgroup's non-empty items (the end: one past them)
   Item it;
   bool valid;
 };
@@ -648,6 +649,7 @@ __device__ __forceinline__ bool item_at(const Grid &g, int k, const int32_t *cu,
 }
 // The next item with at least one chunk after round W.k; W.valid = false past the last.
 __device__ __forceinline__ void next_item(Walker &W, const Grid &g, const int32_t *cu) {
+  ++W.ord;
   for (;;) {
     ++W.k;
     if (!item_at(g, W.k, cu, W.it)) {
@@ -664,6 +666,7 @@ __device__ __forceinline__ void next_item(Walker &W, const Grid &g, const int32_
 __device__ __forceinline__ Walker first_step(const Grid &g, const int32_t *cu) {
   Walker W;
   W.k = -1;
+  W.ord = -1;
   next_item(W, g, cu);
   return W;
 }
@@ -678,17 +681,81 @@ __device__ __forceinline__ void next_step_clamped(Walker &W, const Grid &g, cons
   if (t.valid) W = t;
 }
 
+// Item ring.  The prefetch wave, whose walker runs kPrefetchAhead - 1 steps ahead, publishes each
+// item it enters (and, past the last, an end marker) in LDS slot ord % kRingItems; the other waves
+// take their items from there inside the loop.  Their own walk would load cu (and h0_index) with
+// scalar loads at every change of item, and those loads sat on the chain (measured on 7 sequences
+// of about 97 tokens: an item's first and last chunk steps took 1.4x and 1.3x a middle one).  A
+// slot is rewritten kRingItems items after it was written, when every wave has moved past its item.
+// Slot: k, n, h, hk, tb, te, nc, and the row of the initial-state pool the item starts from
+// (-1: zeros).
+constexpr int kRingItems = 8;
+constexpr int kRingWords = 8;
+__device__ __forceinline__ int h0_row(int n, const float *h0, const int32_t *h0_index, int num_h0) {
+  if (!h0) return -1;
+  const int r = h0_index ? h0_index[n] : n;
+  return r >= 0 && r < num_h0 ? r : -1;
+}
+// Writes W's item (or the end marker) into its slot; lane 0 stores.  The caller waits for the
+// store (lgkmcnt) before the barrier after which other waves read the slot.
+__device__ __forceinline__ void ring_publish(int *ring, const Walker &W, const float *h0,
+                                             const int32_t *h0_index, int num_h0, int l) {
+  int4 a, b;
+  a.x = W.k;
+  if (W.valid) {
+    a.y = W.it.n;
+    a.z = W.it.h;
+    a.w = W.it.hk;
+    b.x = W.it.tb;
+    b.y = W.it.te;
+    b.z = W.it.nc;
+    b.w = h0_row(W.it.n, h0, h0_index, num_h0);
+  } else {
+    a.y = -1;
+    a.z = a.w = b.x = b.y = b.z = b.w = 0;
+  }
+  if (l == 0) {
+    int4 *p = reinterpret_cast<int4 *>(ring + kRingWords * (W.ord % kRingItems));
+    p[0] = a;
+    p[1] = b;
+  }
+}
+// Item ord from the ring (chunk 0); h0r: its initial-state row.
+__device__ __forceinline__ void ring_item(Walker &W, int &h0r, const int *ring, int ord) {
+  const int4 *p = reinterpret_cast<const int4 *>(ring + kRingWords * (ord % kRingItems));
+  const int4 a = p[0], b = p[1];
+  W.ord = ord;
+  W.c = 0;
+  W.k = __builtin_amdgcn_readfirstlane(a.x);
+  W.it.n = __builtin_amdgcn_readfirstlane(a.y);
+  W.it.h = __builtin_amdgcn_readfirstlane(a.z);
+  W.it.hk = __builtin_amdgcn_readfirstlane(a.w);
+  W.it.tb = __builtin_amdgcn_readfirstlane(b.x);
+  W.it.te = __builtin_amdgcn_readfirstlane(b.y);
+  W.it.nc = __builtin_amdgcn_readfirstlane(b.z);
+  h0r = __builtin_amdgcn_readfirstlane(b.w);
+  W.it.slot0 = W.it.tb / kChunk + W.it.n;
+  W.valid = W.it.n >= 0;
+}
+__device__ __forceinline__ void next_step_ring(Walker &W, const int *ring) {
+  if (++W.c == W.it.nc) {
+    int h0r;
+    ring_item(W, h0r, ring, W.ord + 1);
+  }
+}
+__device__ __forceinline__ void next_step_ring_clamped(Walker &W, const int *ring) {
+  Walker t = W;
+  next_step_ring(t, ring);
+  if (t.valid) W = t;
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Initial state slice of item it for compute wave w (H[a][rr] = state row state_key(w, a,
 // 4 lg + rr), column d0 + lj): h0[h0_index[n]] of the pool, zeros outside [0, num_h0), h0[n]
 // without an index, zeros without h0.
-__device__ __forceinline__ void load_h0(f32x4 (&H)[2], const Item &it, const float *h0,
-                                        const int32_t *h0_index, int num_h0, int Hv, int d0,
-                                        int w, int l) {
-  const float *h0s = nullptr;
-  if (h0) {
-    const int r = h0_index ? h0_index[it.n] : it.n;
-    if (r >= 0 && r < num_h0) h0s = h0 + ((size_t)r * Hv + it.h) * kDim * kDim;
-  }
+__device__ __forceinline__ void load_h0_row(f32x4 (&H)[2], int r, int h, const float *h0, int Hv,
+                                            int d0, int w, int l) {
+  const float *h0s = r >= 0 ? h0 + ((size_t)r * Hv + h) * kDim * kDim : nullptr;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -697,21 +764,35 @@ __device__ __forceinline__ void load_h0(f32x4 (&H)[2], const Item &it, const flo
       H[a][rr] = h0s ? h0s[(size_t)key * kDim + d0 + (l & 15)] : 0.f;
     }
 }
+__device__ __forceinline__ void load_h0(f32x4 (&H)[2], const Item &it, const float *h0,
+                                        const int32_t *h0_index, int num_h0, int Hv, int d0,
+                                        int w, int l) {
+  int r = -1;
+  if (h0) {
+    r = h0_index ? h0_index[it.n] : it.n;
+    if (r < 0 || r >= num_h0) r = -1;
+  }
+  load_h0_row(H, r, it.h, h0, Hv, d0, w, l);
+}
 __device__ __forceinline__ void store_ht(const f32x4 (&H)[2], const Item &it, float *hT, int Hv,
                                          int d0, int w, int l) {
   if (!hT) return;
-  float *dst = hT + ((size_t)it.n * Hv + it.h) * kDim * kDim + d0 + (l & 15);
+  // a uniform base and 32-bit lane offsets that do not change from item to item
+  unsigned char *base = reinterpret_cast<unsigned char *>(hT + ((size_t)it.n * Hv + it.h) * kDim * kDim);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      __builtin_nontemporal_store(H[a][rr], dst + (size_t)state_key(w, a, 4 * (l >> 4) + rr) * kDim);
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t off = 4u * (uint32_t)(state_key(w, a, 4 * (l >> 4) + rr) * kDim + d0 + (l & 15));
+      __builtin_nontemporal_store(H[a][rr], reinterpret_cast<float *>(base + off));
+    }
 }
 // The compute waves' walk to the next non-empty item: an empty sequence's final state is its
 // initial state, copied here.
 __device__ __forceinline__ void next_item_copying(Walker &W, const Grid &g, const int32_t *cu,
                                                   const float *h0, const int32_t *h0_index,
                                                   int num_h0, float *hT, int d0, int w, int l) {
+  ++W.ord;
   for (;;) {
     ++W.k;
     if (!item_at(g, W.k, cu, W.it)) {
@@ -992,6 +1073,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char Uo[kXBytes];
   __shared__ __attribute__((aligned(16))) unsigned char ostage[kComputeWaves * kOBytes];
   __shared__ __attribute__((aligned(16))) unsigned int touch_sink[64];
+  __shared__ __attribute__((aligned(16))) int ring[kRingItems * kRingWords];
 
   const Grid gr{(int)gridDim.x, total_items, Hv, Hv / Hk};
   const int tile = (int)(((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) % kDvTiles);  // every round
@@ -1004,34 +1086,52 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
     // Prefetch wave: warms L2 kPrefetchAhead steps ahead of use and never waits for its loads
     // inside the loop (so a slow line holds up nothing).  Barriers as the compute waves.  Of a
     // sequence's partial last chunk only the rows that exist are warmed (items of short sequences
-    // are mostly such chunks).
+    // are mostly such chunks).  Its walker pf, the step warmed next, runs kPrefetchAhead - 1 steps
+    // ahead and publishes every item it enters, and the end, in the ring.  The walk (scalar loads
+    // of cu and h0_index at item changes) is done between b1 and b2, where this wave has nothing
+    // else to do; before b1 it only issues the step's loads.
     Walker cur = first_step(gr, cu);
     if (cur.valid) {
       const unsigned sink = (unsigned)(uintptr_t)touch_sink;
-      Walker pf = cur;  // the step warmed next: steps 2 .. kPrefetchAhead - 1 first
-      next_step(pf, gr, cu);
-      if (pf.valid) next_step(pf, gr, cu);
-      dma_barrier();
-      PrefetchLane pl;  // lines of chunk 0 of item round pl_k
-      int pl_k = -1;
-      for (int s = 0; cur.valid; ++s) {
-        for (int cnt = s == 0 ? kPrefetchAhead - 2 : 1; cnt > 0 && pf.valid; --cnt) {
-          const Item &it = pf.it;
-          if (pl_k != pf.k) {
-            pl = prefetch_lanes(it.tb, it.slot0, it.hk, it.h, Hk, Hv, tile, tile * r + it.h - it.hk * r,
-                                kDvTiles * r, l, q, k, v, rec);
-            pl_k = pf.k;
-          }
-          const int rows = min(kChunk, it.te - it.tb - kChunk * pf.c);  // rows of this chunk
+      Walker pf = cur;
+      PrefetchLane pl;  // lines of chunk 0 of pf's item
+      auto enter = [&]() {  // pf has entered an item, or the end
+        ring_publish(ring, pf, h0, h0_index, num_h0, l);
+        if (pf.valid)
+          pl = prefetch_lanes(pf.it.tb, pf.it.slot0, pf.it.hk, pf.it.h, Hk, Hv, tile,
+                              tile * r + pf.it.h - pf.it.hk * r, kDvTiles * r, l, q, k, v, rec);
+      };
+      auto advance = [&]() {
+        next_step(pf, gr, cu);
+        if (!pf.valid || pf.c == 0) enter();
+      };
+      auto warm = [&]() {  // step pf's lines
+        const int rows = min(kChunk, pf.it.te - pf.it.tb - kChunk * pf.c);  // rows of this chunk
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            if (pl.ptr[j] && pl.row[j] < rows) touch(pl.ptr[j] + (size_t)pf.c * pl.adv[j], sink);
-          next_step(pf, gr, cu);
-        }
-        dma_barrier();
-        dma_barrier();
-        dma_barrier();
-        next_step(cur, gr, cu);
+        for (int j = 0; j < 2; ++j)
+          if (pl.ptr[j] && pl.row[j] < rows) touch(pl.ptr[j] + (size_t)pf.c * pl.adv[j], sink);
+      };
+      // steps 0 .. 2 into the ring before the first barrier; steps 2 .. kPrefetchAhead - 2 warmed
+      // and steps 3 .. kPrefetchAhead - 1 published before b1 of step 0
+      enter();
+      advance();
+      if (pf.valid) advance();
+      wait_lgkmcnt0();
+      dma_barrier();
+      for (int cnt = kPrefetchAhead - 3; cnt > 0 && pf.valid; --cnt) {
+        warm();
+        advance();
+      }
+      wait_lgkmcnt0();
+      for (int s = 0; cur.valid; ++s) {
+        // step s + kPrefetchAhead - 1 warmed before b1; step s + kPrefetchAhead entered after b1
+        if (pf.valid) warm();
+        dma_barrier();  // b1
+        if (pf.valid) advance();
+        wait_lgkmcnt0();
+        dma_barrier();  // b2
+        dma_barrier();  // b3
+        next_step_ring(cur, ring);
       }
     }
     wait_vmcnt<0>();  // no LDS write may land after the workgroup ends
@@ -1059,7 +1159,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         __syncthreads();  // b2
         out_stage(O, pf, out_fetch(decs + (s % kDecStages) * kDecBytes, Uo, ow, l), ow, l, oslot);
         const int c_ = cur.c, tb_ = cur.it.tb, te_ = cur.it.te, h_ = cur.it.h;
-        next_step(cur, gr, cu);
+        next_step_ring(cur, ring);
         if (cur.valid) load_p(pf, rec_at(rec, cur.it.slot0 + cur.c, cur.it.h, Hv), ow, l);
         store_o<kONt>(c_, tb_, te_, Hv, ow, l, oslot, reinterpret_cast<unsigned char *>(o + (size_t)h_ * kDim + d0),
                       ooff);
@@ -1103,7 +1203,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         // Step s + 2 is loaded during step s, spread over its three phases, into tile and decay
         // slots (s + 2) % 3, which held step s - 1 (clamped reloads of the last step only go to
         // slots that are no longer read): K before b1, Q before b2, V and the decays before b3.
-        next_step_clamped(ld, gr, cu);
+        next_step_ring_clamped(ld, ring);
         const unsigned tslot = tiles_lds + ((s + 2) % kTileStages) * kTileBytes;
         const uint8_t *tp = rec_at(rec, ld.it.slot0 + ld.c, ld.it.h, Hv);
         dma_tiles<0>(ld.c, ld.it.tb, ld.it.te, Hk, Hv, pw, l, GDN_BASES(ld), tp, pl, tslot);
@@ -1118,7 +1218,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
         if (pw == kDecWave)
           dma_dec(ld.it.slot0 + ld.c, ld.it.h, Hv, l, rec, decs_lds + ((s + 2) % kDecStages) * kDecBytes);
         dma_barrier();  // b3
-        next_step(cur, gr, cu);
+        next_step_ring(cur, ring);
       }
 #undef GDN_BASES
     }
@@ -1128,38 +1228,62 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_multi_kernel(
 
   // Compute waves.  State slice: H[a][rr] = H[key state_key(w, a, 4 lg + rr)][value d0 + lj].
   // At the last chunk of an item the final state is stored and the next item's initial state,
-  // loaded from the item's first chunk on (items of short sequences last one or two chunks, less
-  // than a load from memory), takes its place before H (hi and lo) goes to LDS.
+  // loaded kPrefetchAhead - 1 chunks earlier (or from the item's first chunk on: items of short
+  // sequences last one or two chunks, less than a load from memory), takes its place before H (hi
+  // and lo) goes to LDS.
   Walker cur;
   cur.k = -1;
+  cur.ord = -1;
   next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
   if (!cur.valid) return;
   f32x4 H[2], Hn[2];
   load_h0(H, cur.it, h0, h0_index, num_h0, Hv, d0, w, l);
+  Walker nx = cur;  // the next item: the second by the walk, later ones from the ring
+  next_item(nx, gr, cu);
+  if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
   write_ht(Ht, Htl, H, w, l);
   __syncthreads();
   bf16x8 ka[2][2];
   read_k_rows(ka, tiles, w, l);
+  // Hf: the final state of the last item, whose registers the stores read after they issue.  It
+  // stays live over the loop, so that no register of it is rewritten (which would wait for the
+  // stores, and so for every load issued after them) before the next item's end.
+  f32x4 Hf[2] = {};
   for (int s = 0; cur.valid; ++s) {
+    asm volatile("" ::"v"(Hf[0]), "v"(Hf[1]));
     const bool last = cur.c == cur.it.nc - 1;
-    if (cur.c == 0) {
-      Walker nx = cur;
-      next_item(nx, gr, cu);  // the next item's initial state (copies of empty items come later)
-      if (nx.valid) load_h0(Hn, nx.it, h0, h0_index, num_h0, Hv, d0, w, l);
+    // The ring holds the next item from kPrefetchAhead - 1 steps before its first chunk on.
+    if (cur.ord > 0 && cur.c == max(0, cur.it.nc - (kPrefetchAhead - 1))) {
+      int h0r;
+      ring_item(nx, h0r, ring, cur.ord + 1);
+      if (nx.valid) load_h0_row(Hn, h0r, nx.it.h, h0, Hv, d0, w, l);
     }
     chunk_step<false>(tiles + (s % kTileStages) * kTileBytes, tiles + ((s + 1) % kTileStages) * kTileBytes,
                       decs + (s % kDecStages) * kDecBytes, w, l, ka, H, Ht, Htl, Rh, Rl, Uh, Ul, Uo);
     if (last) {
-      store_ht(H, cur.it, hT, Hv, d0, w, l);
-      next_item_copying(cur, gr, cu, h0, h0_index, num_h0, hT, d0, w, l);
-      if (cur.valid) {
+      // The next item's state goes to LDS before this one's final state is stored: a wait for its
+      // loads placed after the stores would wait for the stores too.
 #pragma unroll
-        for (int a = 0; a < 2; ++a) H[a] = Hn[a];
+      for (int a = 0; a < 2; ++a) {
+        Hf[a] = H[a];
+        if (nx.valid) H[a] = Hn[a];
       }
+      write_ht(Ht, Htl, H, w, l);
+      __builtin_amdgcn_sched_barrier(0);
+      store_ht(Hf, cur.it, hT, Hv, d0, w, l);
+      // empty items between this one and the next: their final state is their initial one
+      for (int kk = cur.k + 1; kk < nx.k; ++kk) {
+        Item e;
+        item_at(gr, kk, cu, e);
+        f32x4 Hc[2];
+        load_h0(Hc, e, h0, h0_index, num_h0, Hv, d0, w, l);
+        store_ht(Hc, e, hT, Hv, d0, w, l);
+      }
+      cur = nx;
     } else {
       ++cur.c;
+      write_ht(Ht, Htl, H, w, l);
     }
-    write_ht(Ht, Htl, H, w, l);
     __syncthreads();  // b3
   }
 }
