@@ -2,10 +2,10 @@
 //
 // The "open-jev-fast" README ("Phase 2", item 1) has one fused kernel for the work before the
 // Gated DeltaNet rule (the convolution, its SiLU, the q/k/v split and normalisation) and one for
-// the gated norm after it; by "Phase 3" item 3 q and k stay at the 16 key heads.  Both kernels here are HBM-bound streams: 16-byte
-// vector loads and stores, fp32 math (SiLU and the norms' reciprocal square roots on the hardware
-// exp2 / rcp / rsq units: the outputs are bf16), and the per-row reductions as 16-lane
-// butterflies inside a wave (no LDS).
+// the gated norm after it; by "Phase 3" item 3 q and k stay at the 16 key heads.  Both kernels
+// here are HBM-bound streams: 16-byte vector loads and stores, fp32 math (SiLU and the norms'
+// reciprocal square roots on the hardware exp2 / rcp / rsq units: the outputs are bf16), and the
+// per-row reductions as 16-lane butterflies inside a wave (no LDS).
 #include "gdn_device.h"
 
 namespace gdn {

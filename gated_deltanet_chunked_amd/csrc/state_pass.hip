@@ -1,10 +1,10 @@
 // state_pass.hip -- the sequential inter-chunk state pass fused with the chunk output.
 //
 // As in the fused kernel of the "open-jev-fast" README ("Phase 3", item 1), the fp32 recurrent
-// state stays on chip and is all that one chunk hands to the next.  Here one workgroup owns one (sequence, v-head,
-// 16-column slice of the 128 value columns): the state slice H[:, cols] (128 x 16 fp32) lives in
-// MFMA accumulators, spread over 4 compute waves (32 key rows each, see state_key), and the
-// chunks of the sequence are walked in order.  Sequences, heads and slices run in parallel.
+// state stays on chip and is all that one chunk hands to the next.  Here one workgroup owns one
+// (sequence, v-head, 16-column slice of the 128 value columns): the state slice H[:, cols]
+// (128 x 16 fp32) lives in MFMA accumulators, spread over 4 compute waves (32 key rows each, see
+// state_key), and the chunks of the sequence are walked in order.  Sequences, heads and slices run in parallel.
 //
 // With H = S^T (key-major), local cumsum G, T' = (I + A)^-1 diag(beta) and
 // P = tril(Q K^T o e^{G_i - G_j}) from chunk_prep.hip, one chunk is
@@ -163,8 +163,9 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const void *p) {
 }
 
 // Producers.  Per chunk the four producer waves issue the K and Q tiles (16 instructions each),
-// the V tile (2), the T' fragments of the record (12) and its decays (one, half a wave).  Wave pw's share is fixed -- tile rows 4m .. 4m + 3 for m = pw mod 4, and
-// the V tile on wave 3 -- so the vmcnt bookkeeping is static.  Rows past the sequence end are
+// the V tile (2), the T' fragments of the record (12) and its decays (one, half a wave).  Wave
+// pw's share is fixed -- tile rows 4m .. 4m + 3 for m = pw mod 4, and the V tile on wave 3 -- so
+// the vmcnt bookkeeping is static.  Rows past the sequence end are
 // clamped to its last row, which the compute waves never use.
 constexpr int kDmaTp = kTpBytes / 1024;                   // 12: T' KiB m on wave m % 4
 __host__ __device__ constexpr int kTileCount(int pw) { return 8 + kDmaTp / 4 + (pw == 3 ? kDmaV : 0); }
