@@ -22,7 +22,8 @@
  *    last HIP error.  All work is enqueued on the caller's `stream` (NULL = the default stream).
  *  * Layouts are row-major and contiguous.  bf16 tensors are raw 16-bit bf16 values.
  *      q, k    : bf16 [T, Hk, dk]          v : bf16 [T, Hv, dv]
- *      g, beta : fp32 [T, Hv]   (g is the log-decay, one value per token per v-head)
+ *      g, beta : fp32 [T, Hv]   (g is the log-decay, one value per token per v-head, <= 0;
+ *                                values below -40, a decay of e^-40 = 4e-18, act as -40)
  *      cu_seqlens : int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = T
  *      h0, hT  : fp32 [N, Hv, dk, dv], key-major: element [n][h][i][j] = S[j][i] (H = S^T)
  *      o       : bf16 [T, Hv, dv]

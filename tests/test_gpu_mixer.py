@@ -144,7 +144,7 @@ def test_mixer_head_ratios(Hk, Hv):
     check_mixer(*run_mixer_gpu(m, Hk, Hv), *run_mixer_oracle(m, Hk, Hv), f"Hk={Hk} Hv={Hv}", m)
 
 
-@pytest.mark.parametrize("case", ["t936", "varlen_ratio1", "varlen_ratio3"])
+@pytest.mark.parametrize("case", ["t936", "varlen_ratio1", "varlen_ratio3", "extreme"])
 def test_mixer_gates(case):
     # gdn_mixer_fwd_gates: g = -exp(A_log) softplus(a + dt_bias) and beta = sigmoid(b) made in the
     # mixer's first kernel (fp32 on the GPU), against the oracle's gates (fp64) fed to the mixer
@@ -154,10 +154,21 @@ def test_mixer_gates(case):
         m, Hk, Hv = gi.make_mixer_inputs(100), 16, 32
     elif case == "varlen_ratio1":
         m, Hk, Hv = gi.make_mixer_inputs(11, lengths=[70, 1, 200, 33], Hk=2, Hv=2, with_h0=True), 2, 2
-    else:
+    elif case == "varlen_ratio3":
         m, Hk, Hv = gi.make_mixer_inputs(12, lengths=[129, 64, 5], Hk=1, Hv=3), 1, 3
+    else:
+        m, Hk, Hv = gi.make_mixer_inputs(13, lengths=[150, 70], Hk=2, Hv=4, with_h0=True), 2, 4
     T = m.qkv.shape[0]
     gt = gi.make_gate_inputs(200, T, Hv)
+    if case == "extreme":
+        # softplus far in both tails (a + dt_bias up to +-120: the decay saturates, e^g underflows
+        # to zero and the state restarts; or softplus underflows and the state is kept), beta at
+        # 0 and 1 (b = -+90), and decay rates A from 1e-3 to 1e3
+        rng = np.random.default_rng(201)
+        a = rng.choice([-120.0, -40.0, -3.0, 0.0, 3.0, 40.0, 120.0], size=(T, Hv))
+        b = rng.choice([-90.0, -8.0, 0.0, 8.0, 90.0], size=(T, Hv))
+        gt = gi.GateInputs(gi.bf16_bits(a), gi.bf16_bits(b),
+                           np.log(np.array([1e-3, 1.0, 30.0, 1e3][:Hv])).astype(np.float32), gt.dt_bias)
     say(f"[mixer-gates] {case} Hk={Hk} Hv={Hv} T={T}")
     f = gi.bits_to_f64
     g, beta = oracle.gates(f(gt.a), f(gt.b), gt.A_log.astype(np.float64), gt.dt_bias.astype(np.float64))

@@ -164,6 +164,22 @@ def test_extreme_gates():
     check(o, hT, *run_oracle(x), "extreme gates")
 
 
+def test_huge_log_decays():
+    # Spikes of g far below any fp32 resolution of the decay (-1e3 .. -1e6) amid slow decay: the
+    # chunk's later decays are differences of cumsums that the spikes made huge, which the prep
+    # bounds by flooring g (a decay of e^-40 per token already clears the state).
+    say("[huge-g] g spikes of -1e3 .. -1e6 amid g ~ -0.01, beta in {0, 1}")
+    x = gi.make_gdn_inputs(2, 4, [150, 200], seed=112, with_h0=True)
+    rng = np.random.default_rng(113)
+    x.g[:] = -0.01 * rng.random(x.g.shape)
+    spikes = rng.random(x.g.shape) < 0.03
+    x.g[spikes] = -(10.0 ** rng.uniform(3, 6, size=int(spikes.sum())))
+    x.beta[rng.random(x.beta.shape) < 0.1] = 0.0
+    x.beta[rng.random(x.beta.shape) < 0.1] = 1.0
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), "huge log-decays")
+
+
 def test_empty_batch_keeps_state():
     say("[empty] T=0, N=3")
     h0 = (0.1 * np.random.default_rng(3).standard_normal((3, 4, 128, 128))).astype(np.float32)
