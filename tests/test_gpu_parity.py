@@ -153,6 +153,16 @@ def test_head_ratios(Hk, Hv):
     check(o, hT, *run_oracle(x), f"Hk={Hk} Hv={Hv}")
 
 
+@pytest.mark.parametrize("Hk,Hv", [(1, 1), (1, 2), (1, 3), (2, 2)])
+def test_time_split_few_heads(Hk, Hv):
+    # One sequence of 2,000 tokens (32 chunks) at 1-3 v-heads: the pass splits it in time (4 to 8
+    # segments, each segment's state carried by the scan), with an odd head count among them.
+    say(f"[split-heads] T=2000 Hk={Hk} Hv={Hv} with h0")
+    x = gi.make_gdn_inputs(Hk, Hv, [2000], seed=120 + 10 * Hk + Hv, with_h0=True)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), f"split Hk={Hk} Hv={Hv}")
+
+
 def test_extreme_gates():
     say("[extreme] g=-30 spikes, beta in {0, 1}")
     x = gi.make_gdn_inputs(2, 4, [200], seed=110, with_h0=True)
