@@ -163,6 +163,54 @@ def test_time_split_few_heads(Hk, Hv):
     check(o, hT, *run_oracle(x), f"split Hk={Hk} Hv={Hv}")
 
 
+def test_exact_retrieval():
+    # Keys distinct standard basis vectors, g = 0, beta = 1, no initial state: the state after token
+    # t is sum_{s <= t} v_s k_s^T, so the query q_t = k_t retrieves o_t = v_t exactly (a closed form
+    # of the rule, not the oracle).  Two sequences of 128 and 77 tokens (two and two chunks) with the
+    # keys in a shuffled order.
+    say("[retrieval] orthonormal keys, g = 0, beta = 1, q_t = k_t: o = v")
+    lengths = [128, 77]
+    x = gi.make_gdn_inputs(1, 1, lengths, seed=130)
+    rng = np.random.default_rng(131)
+    eye = np.eye(128)
+    for n, L in enumerate(lengths):
+        keys = eye[rng.permutation(128)[:L]]
+        sl = slice(x.cu[n], x.cu[n + 1])
+        x.k[sl, 0] = gi.bf16_bits(keys)
+        x.q[sl, 0] = gi.bf16_bits(keys)
+    x.g[:] = 0.0
+    x.beta[:] = 1.0
+    o, hT = run_gpu(x)
+    v = gi.bits_to_f64(x.v)
+    r = rel_l2(o, v)
+    say(f"  retrieval: o vs v rel-L2 {r:.3e}, max-abs {np.abs(o - v).max():.3e}")
+    assert r <= 2.0 ** -8, f"o vs v rel-L2 {r}"
+    check(o, hT, *run_oracle(x), "retrieval vs oracle")
+
+
+def test_pure_decay():
+    # beta = 0: no update, the state only decays (a closed form of the rule): with G_t the cumsum of
+    # g from the sequence start, o_t = e^{G_t} H0^T q_t and hT = e^{G_T} H0 (H0 key-major).
+    say("[pure-decay] beta = 0: o_t = e^G_t H0^T q_t, hT = e^G_T H0")
+    lengths = [150, 64, 1]
+    x = gi.make_gdn_inputs(2, 4, lengths, seed=132, with_h0=True, h0_std=0.5)
+    x.beta[:] = 0.0
+    o, hT = run_gpu(x)
+    q = gi.bits_to_f64(x.q)
+    o_cf = np.zeros_like(o)
+    h_cf = np.zeros_like(hT)
+    for n in range(len(lengths)):
+        sl = slice(x.cu[n], x.cu[n + 1])
+        G = np.cumsum(x.g[sl].astype(np.float64), axis=0)  # [L, Hv]
+        for h in range(4):
+            H0 = x.h0[n, h].astype(np.float64)
+            o_cf[sl, h] = np.exp(G[:, h])[:, None] * (q[sl, h // 2] @ H0)
+            h_cf[n, h] = np.exp(G[-1, h]) * H0
+    ro, rh = rel_l2(o, o_cf), rel_l2(hT, h_cf)
+    say(f"  pure decay vs closed form: o rel-L2 {ro:.3e} | hT rel-L2 {rh:.3e}")
+    assert ro <= O_REL and rh <= 1e-5
+
+
 def test_extreme_gates():
     say("[extreme] g=-30 spikes, beta in {0, 1}")
     x = gi.make_gdn_inputs(2, 4, [200], seed=110, with_h0=True)
