@@ -153,6 +153,17 @@ def test_head_ratios(Hk, Hv):
     check(o, hT, *run_oracle(x), f"Hk={Hk} Hv={Hv}")
 
 
+@pytest.mark.parametrize("Hk,Hv,T", [(16, 64, 300), (8, 40, 200)])
+def test_many_heads_one_sequence(Hk, Hv, T):
+    # More (v-head, column tile) items than workgroups on the device from a single sequence: the
+    # persistent pass walks several heads per workgroup; Hv = 40 also leaves the prep's head pairs
+    # (20) off the XCD dealing, which needs a multiple of 8.
+    say(f"[many-heads] T={T} Hk={Hk} Hv={Hv} with h0")
+    x = gi.make_gdn_inputs(Hk, Hv, [T], seed=140 + Hv, with_h0=True)
+    o, hT = run_gpu(x)
+    check(o, hT, *run_oracle(x), f"Hk={Hk} Hv={Hv} T={T}")
+
+
 @pytest.mark.parametrize("Hk,Hv", [(1, 1), (1, 2), (1, 3), (2, 2)])
 def test_time_split_few_heads(Hk, Hv):
     # One sequence of 2,000 tokens (32 chunks) at 1-3 v-heads: the pass splits it in time (4 to 8
