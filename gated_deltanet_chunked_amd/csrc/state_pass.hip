@@ -692,6 +692,10 @@ __device__ __forceinline__ void next_step_clamped(Walker &W, const Grid &g, cons
 // (-1: zeros).
 constexpr int kRingItems = 8;
 constexpr int kRingWords = 8;
+// During step s the prefetch wave writes items up to cur + kPrefetchAhead (cur: the item of step
+// s), into the slot of the item kRingItems before, while the other waves still read items from cur
+// on: that earlier item must be older than cur.
+static_assert(kRingItems > kPrefetchAhead, "a ring slot would be rewritten while still read");
 __device__ __forceinline__ int h0_row(int n, const float *h0, const int32_t *h0_index, int num_h0) {
   if (!h0) return -1;
   const int r = h0_index ? h0_index[n] : n;
