@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_last_hip_error"
                     "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd", "gdn_chunk_fwd_indexed",
                     "gdn_chunk_fwd_noalloc", "gdn_chunk_prep",
                     "gdn_state_pass", "gdn_mixer_fwd_workspace_size", "gdn_mixer_fwd", "gdn_mixer_fwd_cont",
-                    "gdn_mixer_fwd_fused_norm", "gdn_mixer_fwd_gates")
+                    "gdn_mixer_fwd_fused_norm", "gdn_mixer_fwd_gates", "gdn_mixer_fwd_gates_cont")
 
 
 class ChunkDesc(ctypes.Structure):
@@ -102,6 +102,8 @@ def lib():
         L.gdn_mixer_fwd_gates.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 13
         L.gdn_mixer_fwd_cont.restype = ctypes.c_int
         L.gdn_mixer_fwd_cont.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 9 + [ctypes.c_int32] + [P] * 5
+        L.gdn_mixer_fwd_gates_cont.restype = ctypes.c_int
+        L.gdn_mixer_fwd_gates_cont.argtypes = [ctypes.POINTER(MixerDesc)] + [P] * 11 + [ctypes.c_int32] + [P] * 5
         _lib_handle = L
     return _lib_handle
 
@@ -375,6 +377,16 @@ def gdn_mixer_fwd_gates(qkv, conv_w, a, b, A_log, dt_bias, z, norm_w, cu_seqlens
     return y, hT
 
 
+def gdn_mixer_fwd_gates_cont(qkv, conv_w, a, b, A_log, dt_bias, z, norm_w, cu_seqlens, h0=None, conv_in=None,
+                             state_index=None, *, Hk=16, Hv=32, y=None, hT=None, conv_out=None, want_state=True,
+                             want_window=True, norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
+    """gdn_mixer_fwd_cont with the gate parameters made in the mixer's first kernel, as in
+    gdn_mixer_fwd_gates.  Returns (y, hT, conv_out)."""
+    return _mixer(qkv, conv_w, None, None, z, norm_w, cu_seqlens, h0, conv_in, state_index, True, Hk, Hv, y, hT,
+                  conv_out, want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host, False,
+                  gates=(a, b, A_log, dt_bias))
+
+
 def gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, conv_in=None, state_index=None, *,
                        Hk=16, Hv=32, y=None, hT=None, conv_out=None, want_state=True, want_window=True,
                        norm_eps=1e-6, workspace=None, stream=None, cu_seqlens_host=None):
@@ -438,7 +450,13 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
         raise GdnError(GDN_ERR_SHAPE, "gdn_mixer_fwd_workspace_size")
     workspace = _workspace(workspace, need, dev, fresh)
     m = MixerDesc(_desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), 4, float(norm_eps))
-    if cont:
+    if cont and gates is not None:
+        rc = lib().gdn_mixer_fwd_gates_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(ga), _ptr(gb),
+                                            _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(cu_seqlens),
+                                            _ptr(h0), _ptr(conv_in), S, _ptr(state_index), _ptr(y), _ptr(hT),
+                                            _ptr(conv_out), _stream(stream, dev))
+        where = "gdn_mixer_fwd_gates_cont"
+    elif cont:
         rc = lib().gdn_mixer_fwd_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
                                       _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(conv_in), S, _ptr(state_index),
                                       _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream, dev))

@@ -587,4 +587,15 @@ int gdn_mixer_fwd_gates(const gdn_mixer_desc *d, const void *qkv, const void *co
                    d->chunk.num_seqs, nullptr, y, hT, nullptr, stream, false);
 }
 
+int gdn_mixer_fwd_gates_cont(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, const void *a,
+                             const void *b, const float *A_log, const float *dt_bias, const void *z,
+                             const void *norm_w, const int32_t *cu_seqlens, const float *h0,
+                             const void *conv_in, int32_t num_states, const int32_t *state_index,
+                             void *y, float *hT, void *conv_out, void *stream) {
+  const gdn::GateArgs ga{static_cast<const unsigned short *>(a), static_cast<const unsigned short *>(b),
+                         A_log, dt_bias};
+  return run_mixer(d, qkv, conv_w, nullptr, nullptr, &ga, z, norm_w, cu_seqlens, h0, conv_in, num_states,
+                   state_index, y, hT, conv_out, stream, false);
+}
+
 }  // extern "C"

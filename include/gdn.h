@@ -246,7 +246,8 @@ GDN_EXPORT int gdn_mixer_fwd_fused_norm(const gdn_mixer_desc *d, const void *qkv
  * (Yang, Kautz & Hatamizadeh, ICLR 2025): for token t and v-head h,
  *     g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])     (log-decay, < 0)
  *     beta[t,h] = sigmoid(b[t,h])
- * computed in fp32 (expf / log1pf; softplus without overflow).
+ * computed in fp32 on the hardware exp2, log2 and reciprocal (softplus without overflow, as
+ * max(x, 0) + log(1 + e^-|x|)); g then meets the floor of -40 that every log-decay meets.
  *   a, b          : bf16 [T, Hv] (2-byte aligned) -- the projections' gate rows
  *   A_log, dt_bias: fp32 [Hv] (4-byte aligned)    -- per-head parameters
  * Every other argument, the workspace (gdn_mixer_fwd_workspace_size) and the errors are
@@ -262,7 +263,8 @@ GDN_EXPORT int gdn_mixer_fwd_gates(const gdn_mixer_desc *d, const void *qkv, con
  * The mixer continuing from carried states: beside the recurrent state, each sequence carries
  * the conv input window -- the last conv_taps - 1 rows of qkv before it -- so that both can pass
  * from a prefix to the candidates that continue it (the "open-jev-fast" README, "Phase 2" item 2,
- * keeps the window and the recurrent state of a candidate's path identical to a full run).  C = 2*Hk*dk + Hv*dv, W = conv_taps - 1 (= 3).
+ * keeps the window and the recurrent state of a candidate's path identical to a full run).
+ * C = 2*Hk*dk + Hv*dv, W = conv_taps - 1 (= 3).
  *   h0       : fp32 [num_states, Hv, dk, dv] or NULL (zero states)
  *   conv_in  : bf16 [num_states, W, C] or NULL (zeros before every sequence), oldest row first:
  *              row W-1 is the input just before the sequence's first token
@@ -284,6 +286,21 @@ GDN_EXPORT int gdn_mixer_fwd_cont(const gdn_mixer_desc *d, const void *qkv, cons
                                   const void *conv_in, int32_t num_states,
                                   const int32_t *state_index, void *y, float *hT, void *conv_out,
                                   void *stream);
+
+/*
+ * gdn_mixer_fwd_cont with the gate parameters made in the mixer's first kernel, as in
+ * gdn_mixer_fwd_gates: a continuation (the "open-jev-fast" README, "Phase 2" item 2) of a layer
+ * whose input prep also makes its gates ("Phase 2" item 1).  a, b, A_log and dt_bias replace g
+ * and beta with gdn_mixer_fwd_gates's layouts and checks; every other argument, the workspace and
+ * the errors are gdn_mixer_fwd_cont's.
+ */
+GDN_EXPORT int gdn_mixer_fwd_gates_cont(const gdn_mixer_desc *d, const void *qkv, const void *conv_w,
+                                        const void *a, const void *b, const float *A_log,
+                                        const float *dt_bias, const void *z, const void *norm_w,
+                                        const int32_t *cu_seqlens, const float *h0,
+                                        const void *conv_in, int32_t num_states,
+                                        const int32_t *state_index, void *y, float *hT,
+                                        void *conv_out, void *stream);
 
 #ifdef __cplusplus
 }

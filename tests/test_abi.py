@@ -272,6 +272,39 @@ def test_mixer_cont_validation():
     assert call(z=None) == gdn.GDN_ERR_NULL
 
 
+def test_mixer_gates_cont_validation():
+    # the continued mixer with its gates made in the first kernel: gdn_mixer_fwd_cont's checks with
+    # gdn_mixer_fwd_gates's in place of those of g and beta; every check runs before any launch
+    a = _addrs()
+    ws = gdn.gdn_mixer_fwd_workspace_size(T, N, HK, HV)
+    P = ctypes.c_void_p
+    extra = a["cu"] + GB // 2  # windows, index and the per-head gate parameters, each under 1 MiB
+
+    def call(S=N, **over):
+        b = {"qkv": a["q"], "cw": a["k"], "ga": a["g"], "gb": a["beta"], "A_log": extra + (3 << 20),
+             "dt": extra + (3 << 20) + 256, "z": a["v"], "nw": a["h0"] + GB // 2, "cu": a["cu"], "h0": a["h0"],
+             "cin": extra, "idx": None, "y": a["o"], "hT": a["hT"], "cout": extra + (1 << 20)}
+        b.update(over)
+        pp = lambda x: None if x is None else P(x)
+        m = gdn.MixerDesc(gdn.ChunkDesc(T, N, HK, HV, 128, 128, a["ws"], ws), 4, 1e-6)
+        return gdn.lib().gdn_mixer_fwd_gates_cont(
+            ctypes.byref(m), pp(b["qkv"]), pp(b["cw"]), pp(b["ga"]), pp(b["gb"]), pp(b["A_log"]), pp(b["dt"]),
+            pp(b["z"]), pp(b["nw"]), pp(b["cu"]), pp(b["h0"]), pp(b["cin"]), S, pp(b["idx"]), pp(b["y"]),
+            pp(b["hT"]), pp(b["cout"]), None)
+
+    idx = extra + (2 << 20)
+    assert call(S=2) == gdn.GDN_ERR_SHAPE                        # pool size must be N without an index
+    for field in ("ga", "gb", "A_log", "dt"):
+        assert call(**{field: None}) == gdn.GDN_ERR_NULL, field
+    assert call(ga=a["g"] + 1) == gdn.GDN_ERR_ALIGN
+    assert call(dt=extra + (3 << 20) + 258) == gdn.GDN_ERR_ALIGN
+    assert call(cin=extra + 8) == gdn.GDN_ERR_ALIGN
+    assert call(S=2, idx=idx, cout=extra) == gdn.GDN_ERR_ALIAS  # in-place window with an index
+    assert call(cout=a["g"]) == gdn.GDN_ERR_ALIAS                # window out over a
+    assert call(hT=extra + (3 << 20)) == gdn.GDN_ERR_ALIAS       # hT over A_log
+    assert call(z=None) == gdn.GDN_ERR_NULL
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(gdn, "_lib_handle", None)

@@ -4,7 +4,10 @@
   many candidates), same tolerance as gdn_chunk_fwd, plus bitwise equality with explicit copies;
 * gdn_mixer_fwd_cont -- the mixer carrying its conv input window beside the recurrent state; the
   window out is bit-exact (copied bf16 values), y and hT to the mixer tolerance, and a split at a
-  chunk boundary continued from its own state and window equals one run bitwise."""
+  chunk boundary continued from its own state and window equals one run bitwise;
+* gdn_mixer_fwd_gates_cont -- the same with the gate parameters made in the first kernel."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -177,3 +180,52 @@ def test_mixer_cont_in_place_and_plain_entry():
     y4, h4, _ = run_cont(m, h0, None, None, 2, 4)
     torch.cuda.synchronize()
     assert torch.equal(y3.view(torch.int16), y4.view(torch.int16)) and torch.equal(h3, h4)
+
+
+def test_mixer_gates_cont_split():
+    # The gates made from the projections, continued across a split at a chunk boundary from the
+    # first part's state and window, equal one gdn_mixer_fwd_gates run bit for bit; a pooled,
+    # indexed continuation against the oracle fed the oracle's gates.
+    lengths = [300, 200]
+    split = 128
+    say(f"[mixer-gates-cont] lengths={lengths} split={split}")
+    m = gi.make_mixer_inputs(290, lengths=lengths, Hk=2, Hv=4, with_h0=True)
+    gt = gi.make_gate_inputs(291, m.qkv.shape[0], 4)
+    dev = lambda rows=None: (bf16_dev(gt.a if rows is None else gt.a[rows]), bf16_dev(gt.b if rows is None else gt.b[rows]),
+                             f32_dev(gt.A_log), f32_dev(gt.dt_bias))
+    y, hT = gdn.gdn_mixer_fwd_gates(bf16_dev(m.qkv), bf16_dev(m.conv_w), *dev(), bf16_dev(m.z), bf16_dev(m.norm_w),
+                                    _i32(m.cu), f32_dev(m.h0), Hk=2, Hv=4,
+                                    cu_seqlens_host=torch.from_numpy(m.cu.astype(np.int64)))
+    cu = m.cu
+    head = np.concatenate([np.arange(cu[n], cu[n] + split) for n in range(2)])
+    tail = np.concatenate([np.arange(cu[n] + split, cu[n + 1]) for n in range(2)])
+
+    def part(rows, cu2, h0, win):
+        c2 = np.asarray(cu2, np.int32)
+        return gdn.gdn_mixer_fwd_gates_cont(bf16_dev(m.qkv[rows]), bf16_dev(m.conv_w), *dev(rows),
+                                            bf16_dev(m.z[rows]), bf16_dev(m.norm_w), _i32(c2), h0, win, None,
+                                            Hk=2, Hv=4, cu_seqlens_host=torch.from_numpy(c2.astype(np.int64)))
+
+    ya, ha, wa = part(head, [0, split, 2 * split], f32_dev(m.h0), None)
+    yb, hb, wb = part(tail, [0, 300 - split, 500 - 2 * split], ha, wa)
+    torch.cuda.synchronize()
+    yy = torch.empty_like(y)
+    yy[torch.from_numpy(head).cuda()] = ya
+    yy[torch.from_numpy(tail).cuda()] = yb
+    assert torch.equal(yy.view(torch.int16), y.view(torch.int16)) and torch.equal(hb, hT), \
+        "a split at a chunk boundary continues bitwise"
+    # pooled states and windows by index, against the oracle with its own gates
+    S, index = 3, np.array([2, -1], np.int32)
+    C = m.qkv.shape[1]
+    h0p, winp = gi.make_state_pool(292, S, 4), gi.make_window_pool(293, S, C)
+    yc, hc, wc = gdn.gdn_mixer_fwd_gates_cont(bf16_dev(m.qkv), bf16_dev(m.conv_w), *dev(), bf16_dev(m.z),
+                                              bf16_dev(m.norm_w), _i32(m.cu), f32_dev(h0p), bf16_dev(winp),
+                                              _i32(index), Hk=2, Hv=4,
+                                              cu_seqlens_host=torch.from_numpy(m.cu.astype(np.int64)))
+    torch.cuda.synchronize()
+    f = gi.bits_to_f64
+    g, beta = oracle.gates(f(gt.a), f(gt.b), gt.A_log.astype(np.float64), gt.dt_bias.astype(np.float64))
+    mg = dataclasses.replace(m, g=g, beta=beta)
+    y_ref, h_ref, w_ref, o_ref = cont_oracle(mg, h0p, winp, index, 2, 4)
+    assert np.array_equal(_np(wc), w_ref), "conv window out (bit-exact)"
+    check_mixer(_np(yc), _np(hc), y_ref, h_ref, o_ref, "gates cont (indexed)", mg)
