@@ -156,13 +156,15 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
 
   // Workgroup b runs on XCD b % 8.  For one sequence the state pass keeps v-heads
   // [x Hv / 8, (x + 1) Hv / 8) on XCD x; dealing the (slot, head group) units out the same way puts
-  // each head's prep on the XCD (and L2) that reads its q and k next.
+  // each head's prep on the XCD (and L2) that reads its q and k next.  An XCD takes its head
+  // groups slot by slot, so the groups of one slot run together and share, in L2, the g and beta
+  // lines (one line holds every v-head of a token) and, with more than two v-heads per k-head, q
+  // and k.
   int slot = blockIdx.x, grp = blockIdx.y;
   if (N == 1 && gridDim.y % 8 == 0) {
-    const int nb = gridDim.x * gridDim.y, bid = blockIdx.y * gridDim.x + blockIdx.x;
-    const int lid = (bid % 8) * (nb / 8) + bid / 8;
-    slot = lid % gridDim.x;
-    grp = lid / gridDim.x;
+    const int bid = blockIdx.y * gridDim.x + blockIdx.x, per = gridDim.y / 8, j = bid / 8;
+    slot = j / per;
+    grp = (bid % 8) * per + j % per;
   }
   const int h_first = grp * HP, hk = h_first / (Hv / Hk);
   const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
