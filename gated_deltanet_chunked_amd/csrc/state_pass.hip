@@ -825,7 +825,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
     const unsigned short *__restrict__ v, const int32_t *__restrict__ cu,
     const float *h0, const int32_t *__restrict__ h0_index, int num_h0,
     unsigned short *__restrict__ o, float *hT,  // hT may equal h0 when h0_index is NULL
-    const uint8_t *__restrict__ rec, int Hk, int Hv, SplitPass sp, NormOut no) {
+    const uint8_t *__restrict__ rec, int Hk, int Hv, int t_one, SplitPass sp, NormOut no) {
   __shared__ __attribute__((aligned(16))) unsigned char tiles[kTileStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char decs[kDecStages * kDecBytes];
   __shared__ __attribute__((aligned(16))) unsigned char Ht[kHtBytes];
@@ -846,9 +846,15 @@ __global__ __launch_bounds__(kThreads, 1) void state_pass_kernel(
   const int d0 = kDvTile * tile;
   const int tid = threadIdx.x, l = tid & 63, lj = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // n is a sequence, or with a time split a segment of sequence 0 (m chunks from chunk m n on)
+  // n is a sequence, or with a time split a segment of sequence 0 (m chunks from chunk m n on).
+  // With one sequence its bounds are 0 and T (t_one), so no load of cu_seqlens precedes the first
+  // tile loads: it would put one more dependent memory round trip before chunk 0 can arrive.
   int tb, te, slot0;
-  if (sp.segs) {
+  if (t_one >= 0) {
+    tb = sp.segs ? min(kChunk * sp.m * n, t_one) : 0;
+    te = sp.segs ? min(tb + kChunk * sp.m, t_one) : t_one;
+    slot0 = sp.segs ? sp.m * n : 0;
+  } else if (sp.segs) {
     tb = min(cu[0] + kChunk * sp.m * n, cu[1]);
     te = min(tb + kChunk * sp.m, cu[1]);
     slot0 = cu[0] / kChunk + sp.m * n;
@@ -1384,6 +1390,7 @@ hipError_t launch_state_pass(const void *q, const void *k, const void *v, const 
   const int total = (sp.segs ? sp.segs : N) * Hv * kDvTiles;
   const int G = total <= max_groups ? total : max_groups;
   const bool o_nt = (uint64_t)T * (uint64_t)Hv * kDim * 2 <= kOStreamBytes;
+  int t_one = N == 1 ? (int)T : -1;  // cu_seqlens = {0, T}
   const unsigned short *q16 = static_cast<const unsigned short *>(q);
   const unsigned short *k16 = static_cast<const unsigned short *>(k);
   const unsigned short *v16 = static_cast<const unsigned short *>(v);
@@ -1395,7 +1402,7 @@ hipError_t launch_state_pass(const void *q, const void *k, const void *v, const 
     if (G != total || sp.segs) return hipErrorInvalidValue;
     NormOut no = *norm;
     void *args[] = {&q16, &k16, &v16, (void *)&cu, (void *)&h0, (void *)&h0_index, &num_h0, &o16, &hT,
-                    &r8, &Hk, &Hv, &sp, &no};
+                    &r8, &Hk, &Hv, &t_one, &sp, &no};
     const void *fn = o_nt ? reinterpret_cast<const void *>(&state_pass_kernel<true, true>)
                           : reinterpret_cast<const void *>(&state_pass_kernel<false, true>);
     return hipLaunchCooperativeKernel(fn, dim3(G), dim3(kThreads), args, 0, stream);
@@ -1404,7 +1411,7 @@ hipError_t launch_state_pass(const void *q, const void *k, const void *v, const 
   if (G == total)
     hipLaunchKernelGGL((o_nt ? state_pass_kernel<true, false> : state_pass_kernel<false, false>), dim3(G),
                        dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0, o16, hT,
-                       r8, Hk, Hv, sp, none);
+                       r8, Hk, Hv, t_one, sp, none);
   else
     hipLaunchKernelGGL(o_nt ? state_pass_multi_kernel<true> : state_pass_multi_kernel<false>,
                        dim3(G), dim3(kThreads), 0, stream, q16, k16, v16, cu, h0, h0_index, num_h0,
