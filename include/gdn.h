@@ -36,8 +36,10 @@
  *    the stream reaches that point.  GDN_ERR_HIP means a launch failed; gdn_last_hip_error()
  *    returns the hipError_t of the calling thread's last such failure.
  *  * The library cannot read cu_seqlens without a device sync, so it trusts that they are
- *    monotone with cu[N] = T (the Python binding checks a host copy).  Zero-length sequences are
- *    allowed: they produce no output rows and hT[n] = h0[n] (or zeros).
+ *    monotone with cu[N] = T (the Python binding checks a host copy).  With N = 1 some kernels
+ *    take the bounds {0, T} from the descriptor instead of reading them, so cu_seqlens must be
+ *    exactly {0, T}.  Zero-length sequences are allowed: they produce no output rows and
+ *    hT[n] = h0[n] (or zeros).
  *  * hT may be exactly h0 (in-place continuation).  Any other overlap of an output with an
  *    input, or of o with hT, is GDN_ERR_ALIAS.
  *  * The workspace is caller-owned device memory of at least *_workspace_size() bytes; its
