@@ -17,7 +17,7 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
 hipError_t launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                              const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                              const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
-                             hipStream_t stream, SplitPass sp, const NormOut *norm);
+                             hipStream_t stream, SplitPass sp, const NormOut *norm, bool o_read_next);
 void launch_state_scan(const float *phi, const float *bend, const float *h0, const int32_t *h0_index,
                        int num_h0, float *hs, int segs, int Hv, hipStream_t stream);
 void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *conv_in,
@@ -209,7 +209,7 @@ gdn::SplitPass plan_split(const Shape &s, int max_groups) {
 int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const void *v,
               const float *g, const float *beta, const int32_t *cu, const StatePool &pool, void *o,
               float *hT, void *ws, hipStream_t stream, const gdn::NormOut *norm = nullptr,
-              const gdn::GateArgs *gates = nullptr) {
+              const gdn::GateArgs *gates = nullptr, bool o_read_next = false) {
   unsigned char *rec = static_cast<unsigned char *>(ws);
   (void)hipGetLastError();  // clear a stale error so that only our launches are reported
   if ((stage & kPrep) && s.T > 0) {
@@ -230,12 +230,12 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
       sp.mode = 0;
       sp.h_out = bend;
       hipError_t e = gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk,
-                                            s.Hv, groups, stream, sp, nullptr);
+                                            s.Hv, groups, stream, sp, nullptr, false);
       if (e != hipSuccess) return record_hip(e);
       sp.mode = 1;
       sp.h_out = phi;
       e = gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, nullptr, rec, s.T, s.N, s.Hk, s.Hv,
-                                 groups, stream, sp, nullptr);
+                                 groups, stream, sp, nullptr, false);
       if (e != hipSuccess) return record_hip(e);
       gdn::launch_state_scan(phi, bend, pool.h0, pool.index, pool.rows, hs, sp.segs, s.Hv, stream);
       e = hipGetLastError();
@@ -244,10 +244,10 @@ int run_chunk(const Shape &s, Stage stage, const void *q, const void *k, const v
       sp.h_in = hs;
       sp.h_out = nullptr;
       return record_hip(gdn::launch_state_pass(q, k, v, cu, nullptr, nullptr, 0, o, hT, rec, s.T, s.N, s.Hk,
-                                               s.Hv, groups, stream, sp, nullptr));
+                                               s.Hv, groups, stream, sp, nullptr, o_read_next));
     }
     return record_hip(gdn::launch_state_pass(q, k, v, cu, pool.h0, pool.index, pool.rows, o, hT, rec, s.T,
-                                             s.N, s.Hk, s.Hv, groups, stream, sp, norm));
+                                             s.N, s.Hk, s.Hv, groups, stream, sp, norm, o_read_next));
   }
   return GDN_OK;
 }
@@ -536,8 +536,9 @@ int run_mixer(const gdn_mixer_desc *d, const void *qkv, const void *conv_w, cons
     if (e != hipSuccess) return record_hip(e);
   }
   const StatePool pool{h0, num_states, state_index};
+  // o is read back by the gated RMSNorm right after the pass: cached stores leave it in L2
   st = run_chunk(s, fused ? kPass : kBoth, qp, kp, vp, g, beta, cu_seqlens, pool, op, hT, base, strm,
-                 fuse_norm ? &norm : nullptr, gates);
+                 fuse_norm ? &norm : nullptr, gates, true);
   if (st != GDN_OK) return st;
   if (tok && !fuse_norm) {
     gdn::launch_gated_rmsnorm(op, z, norm_w, d->norm_eps, s.T, s.Hv, y, strm);

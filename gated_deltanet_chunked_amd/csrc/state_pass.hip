@@ -324,7 +324,8 @@ __device__ __forceinline__ PrefetchLane prefetch_lanes(int tb, int64_t slot0, in
 // nt: streaming (non-temporal) stores, chosen by the host when all of o fits in L2 -- then the
 // dirty o lines would otherwise be written back at the kernel's end, after the last chunk; a
 // larger o is mostly evicted during the kernel anyway, and its 32-byte column slices merge into
-// whole lines in L2 first.
+// whole lines in L2 first.  When the next kernel reads o (the mixer's gated RMSNorm), cached
+// stores keep it in L2 for that kernel whatever its size.
 template <bool kNt>
 __device__ __forceinline__ void store_o(int c, int tb, int te, int Hv, int pw, int l,
                                         const unsigned char *slot, unsigned char *ob, uint32_t ooff) {
@@ -1384,12 +1385,12 @@ void launch_state_scan(const float *phi, const float *bend, const float *h0, con
 hipError_t launch_state_pass(const void *q, const void *k, const void *v, const int32_t *cu,
                              const float *h0, const int32_t *h0_index, int num_h0, void *o, float *hT,
                              const void *rec, int64_t T, int N, int Hk, int Hv, int max_groups,
-                             hipStream_t stream, SplitPass sp, const NormOut *norm) {
+                             hipStream_t stream, SplitPass sp, const NormOut *norm, bool o_read_next) {
   // Items: N Hv 8 (a multiple of 8).  One round when they fit on the device at one workgroup per
   // CU (max_groups, a multiple of 8), else max_groups persistent workgroups.
   const int total = (sp.segs ? sp.segs : N) * Hv * kDvTiles;
   const int G = total <= max_groups ? total : max_groups;
-  const bool o_nt = (uint64_t)T * (uint64_t)Hv * kDim * 2 <= kOStreamBytes;
+  const bool o_nt = !o_read_next && (uint64_t)T * (uint64_t)Hv * kDim * 2 <= kOStreamBytes;
   int t_one = N == 1 ? (int)T : -1;  // cu_seqlens = {0, T}
   const unsigned short *q16 = static_cast<const unsigned short *>(q);
   const unsigned short *k16 = static_cast<const unsigned short *>(k);
