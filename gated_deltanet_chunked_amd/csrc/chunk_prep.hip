@@ -36,6 +36,17 @@ namespace gdn {
 namespace {
 
 constexpr int kPitchF = 68;                        // fp32 row pitch of 64 x 64 LDS matrices
+// Records of at most this many bytes in all are written with cached stores, so that the state pass,
+// which reads them next, finds them in L2; larger ones, which cannot all stay there, with
+// streaming stores (measured both ways at T = 16,384: cached stores made the prep 1.2 us faster
+// and the pass 1.1 us slower).  P is always cached: its 16-byte pieces are written in two halves
+// by different waves and merge in L2.
+constexpr uint64_t kRecStreamBytes = 16u << 20;
+template <typename V>
+__device__ __forceinline__ void rec_store(V *p, V v, bool nt) {
+  if (nt) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 constexpr int kMatBytes = kChunk * kPitchF * 4;    // 17408
 constexpr int kMaxHeads = 2;                       // v-heads per workgroup
 // LDS map: [Ks | Qs] (bf16 64 x 128, swizzled) are dead once the products are in registers, so
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const unsigned short *__restrict__ q, const unsigned short *__restrict__ k,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int Hk, int Hv, uint8_t *__restrict__ rec,
-    ConvArgs ca, GateArgs ga, uint32_t *__restrict__ norm_part) {
+    ConvArgs ca, GateArgs ga, uint32_t *__restrict__ norm_part, bool rec_nt) {
   static_assert(!kConv || HP == 2, "the input prep runs on pairs of v-heads");
   constexpr int kThreads = 64 * kWavesPerHead * HP, kWaves = kWavesPerHead * HP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kConv ? kLdsBytes : kOffW];
@@ -346,8 +357,8 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
       Fcall[kChunk * (3 * x + 1) + l] = l < 32 ? exp_neg(G32 - G) : 0.f;
       Fcall[kChunk * (3 * x + 2) + l] = l < 48 ? exp_neg(G48 - G) : 0.f;
       uint8_t *R = rec_slot + (size_t)(h_first + x) * kRecBytes;
-      __builtin_nontemporal_store(exp_neg(G), reinterpret_cast<float *>(R + kRecEG) + l);
-      __builtin_nontemporal_store(exp_neg(Glast - G), reinterpret_cast<float *>(R + kRecED) + l);
+      rec_store(reinterpret_cast<float *>(R + kRecEG) + l, exp_neg(G), rec_nt);
+      rec_store(reinterpret_cast<float *>(R + kRecED) + l, exp_neg(Glast - G), rec_nt);
     }
   }
   __syncthreads();
@@ -563,8 +574,8 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) split_pair(t[2 * e], t[2 * e + 1], hv[e], lv[e]);
     const u32x4 vh = {hv[0], hv[1], hv[2], hv[3]}, vl = {lv[0], lv[1], lv[2], lv[3]};
-    __builtin_nontemporal_store(vh, reinterpret_cast<u32x4 *>(R + kRecTpHi + f * kFragBytes + ll * 16));
-    __builtin_nontemporal_store(vl, reinterpret_cast<u32x4 *>(R + kRecTpLo + f * kFragBytes + ll * 16));
+    rec_store(reinterpret_cast<u32x4 *>(R + kRecTpHi + f * kFragBytes + ll * 16), vh, rec_nt);
+    rec_store(reinterpret_cast<u32x4 *>(R + kRecTpLo + f * kFragBytes + ll * 16), vl, rec_nt);
   }
 }
 
@@ -576,20 +587,21 @@ void launch_chunk_prep(const void *q, const void *k, const float *g, const float
   const unsigned short *kp = static_cast<const unsigned short *>(k);
   uint8_t *rp = static_cast<uint8_t *>(rec);
   const dim3 pairs((unsigned)nslots, (unsigned)(Hv / 2)), singles((unsigned)nslots, (unsigned)Hv);
+  const bool rec_nt = (uint64_t)nslots * (uint64_t)Hv * kRecBytes > kRecStreamBytes;
   if ((Hv / Hk) % 2 == 0) {  // pairs of v-heads of one k-head per workgroup
     if (gates)
       hipLaunchKernelGGL((chunk_prep_kernel<2, false, true>), pairs, dim3(128 * kWavesPerHead), 0, stream, qp,
-                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part, rec_nt);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<2, false, false>), pairs, dim3(128 * kWavesPerHead), 0, stream, qp,
-                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part, rec_nt);
   } else {
     if (gates)
       hipLaunchKernelGGL((chunk_prep_kernel<1, false, true>), singles, dim3(64 * kWavesPerHead), 0, stream, qp,
-                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part, rec_nt);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<1, false, false>), singles, dim3(64 * kWavesPerHead), 0, stream, qp,
-                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part);
+                         kp, g, beta, cu, (int)T, N, Hk, Hv, rp, ConvArgs{}, ga, norm_part, rec_nt);
   }
 }
 
@@ -605,13 +617,14 @@ void launch_chunk_prep_conv(const void *qkv, const void *conv_w, const void *con
                     static_cast<unsigned short *>(qo), static_cast<unsigned short *>(ko),
                     static_cast<unsigned short *>(vo)};
   const dim3 grid((unsigned)nslots, (unsigned)(Hv / 2));
+  const bool rec_nt = (uint64_t)nslots * (uint64_t)Hv * kRecBytes > kRecStreamBytes;
   const unsigned short *none = nullptr;
   if (gates)
     hipLaunchKernelGGL((chunk_prep_kernel<2, true, true>), grid, dim3(128 * kWavesPerHead), 0, stream, none,
-                       none, g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec), ca, *gates, norm_part);
+                       none, g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec), ca, *gates, norm_part, rec_nt);
   else
     hipLaunchKernelGGL((chunk_prep_kernel<2, true, false>), grid, dim3(128 * kWavesPerHead), 0, stream, none,
-                       none, g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec), ca, GateArgs{}, norm_part);
+                       none, g, beta, cu, (int)T, N, Hk, Hv, static_cast<uint8_t *>(rec), ca, GateArgs{}, norm_part, rec_nt);
 }
 
 }  // namespace gdn
