@@ -237,12 +237,6 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
     const int C = (2 * Hk + Hv) * kDim;
     auto seg_of = [&](int b) { return b == 0 ? hk : (b == 1 ? Hk + hk : 2 * Hk + h_first + b - 2); };
     unsigned short *Ws = reinterpret_cast<unsigned short *>(smem + kOffW);
-    if (tid < 4 * kDim) {  // 8 bytes per thread: the 4 taps of one channel
-      const int b = tid / kDim, ch = tid % kDim;
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      *reinterpret_cast<u32x2 *>(Ws + (b * kDim + ch) * 4) =
-          *reinterpret_cast<const u32x2 *>(ca.conv_w + (size_t)(seg_of(b) * kDim + ch) * 4);
-    }
     const int tfirst = t0 + kTok * tg;
     const unsigned short *win =
         tfirst - 3 < tb ? window_of(ca.conv_in, ca.state_index, ca.num_states, n, (size_t)3 * C) : nullptr;
@@ -256,6 +250,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void chunk_prep_kernel(
       hv[i] = src < tend && (src >= tb || win);
       const unsigned short *row = src >= tb ? ca.qkv + (size_t)src * C : win + (size_t)(src - tb + 3) * C;
       if (hv[i]) xr[i] = *reinterpret_cast<const u16x8 *>(row + ch0);
+    }
+    // The weights after the rows: loaded and stored to LDS first, behind a branch that the
+    // compiler does not move the row loads above, they made the rows wait one memory round trip.
+    if (tid < 4 * kDim) {  // 8 bytes per thread: the 4 taps of one channel
+      const int b = tid / kDim, ch = tid % kDim;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2 *>(Ws + (b * kDim + ch) * 4) =
+          *reinterpret_cast<const u32x2 *>(ca.conv_w + (size_t)(seg_of(b) * kDim + ch) * 4);
     }
     __syncthreads();  // the conv weights are in LDS
     float wt[8][4];
