@@ -137,6 +137,10 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(
   const u16x8 ov = *reinterpret_cast<const u16x8 *>(o + off);
   const u16x8 zv = *reinterpret_cast<const u16x8 *>(z + off);
   const u16x8 wv = *reinterpret_cast<const u16x8 *>(norm_w + chg * 8);
+  // z and the weights are used only under the store's branch, and the compiler would sink their
+  // loads into it, behind the wait for o and the row sum: one more memory round trip.  Used here,
+  // all three loads are in flight together.
+  asm volatile("" ::"v"(zv), "v"(wv));
   float of[8], ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
