@@ -330,3 +330,23 @@ def test_noalloc_scratch_limit():
     d = gdn.ChunkDesc(10, 1, 3, 4, 128, 128, None, 0)  # Hv % Hk != 0
     assert L.gdn_chunk_fwd_noalloc(ctypes.byref(d), *args) == gdn.GDN_ERR_SHAPE
     assert L.gdn_chunk_fwd_noalloc(None, *args) == gdn.GDN_ERR_NULL
+
+
+def test_binding_cu_seqlens_host_check():
+    # The binding checks a host copy of cu_seqlens before any call (the library cannot read it
+    # without a sync): short ones as a Python list, long ones with numpy; every input form.
+    import numpy as np
+    import torch
+
+    T = 936
+    ok = [[0, T], (0, 0, T), torch.tensor([0, T], dtype=torch.int64), torch.tensor([0, 100, T], dtype=torch.int32),
+          np.array([0, 5, 5, T]), torch.arange(0, T + 1, dtype=torch.int64), np.arange(0, T + 1)]
+    for host in ok:
+        assert gdn._check_cu(None, T, host) == len(host) - 1
+    long_bad = torch.arange(0, T + 1, dtype=torch.int64)
+    long_bad[500] = 3  # not monotone, past the short-list path
+    bad = [[0, 5, 3, T], [1, T], [0, T - 1], [0], [], [[0, T]], torch.tensor([[0, T]]), torch.tensor([0, 7, 2, T]),
+           long_bad, long_bad.numpy()]
+    for host in bad:
+        with pytest.raises(ValueError):
+            gdn._check_cu(None, T, host)
