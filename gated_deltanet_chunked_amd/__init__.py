@@ -24,6 +24,7 @@ Layouts (row-major, contiguous): q, k bf16 [T, Hk, 128]; v bf16 [T, Hv, 128]; g,
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -126,11 +127,22 @@ def _desc(T, N, Hk, Hv, ws=None, ws_bytes=0, dk=D, dv=D) -> ChunkDesc:
 
 
 def gdn_chunk_fwd_workspace_size(T: int, N: int, Hk: int, Hv: int) -> int:
-    return int(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(_desc(T, N, Hk, Hv))))
+    return _chunk_ws_size(int(T), int(N), int(Hk), int(Hv))
 
 
 def gdn_mixer_fwd_workspace_size(T: int, N: int, Hk: int, Hv: int, conv_taps: int = 4,
                                  norm_eps: float = 1e-6) -> int:
+    return _mixer_ws_size(int(T), int(N), int(Hk), int(Hv), int(conv_taps), float(norm_eps))
+
+
+# The sizes depend on the shape alone; the calls ask for them every time, so they are kept.
+@functools.lru_cache(maxsize=256)
+def _chunk_ws_size(T, N, Hk, Hv):
+    return int(lib().gdn_chunk_fwd_workspace_size(ctypes.byref(_desc(T, N, Hk, Hv))))
+
+
+@functools.lru_cache(maxsize=256)
+def _mixer_ws_size(T, N, Hk, Hv, conv_taps, norm_eps):
     m = MixerDesc(_desc(T, N, Hk, Hv), conv_taps, norm_eps)
     return int(lib().gdn_mixer_fwd_workspace_size(ctypes.byref(m)))
 
@@ -140,6 +152,8 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _check(t, name, dtype, shape, device):
+    if t.dtype is dtype and t.shape == shape and t.is_contiguous() and t.device == device:
+        return
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -187,6 +201,8 @@ def _keep_for(stream, device, tensors):
     one: tell the caching allocator they are in use on that stream, so that once the caller drops
     them their memory is not handed to a new allocation on the current stream while the call's
     kernels may still be reading or writing it."""
+    if not any(t is not None for t in tensors):
+        return
     ts = _torch_stream(stream, device)
     if ts != torch.cuda.current_stream(device):
         for t in tensors:
