@@ -201,8 +201,8 @@ def _keep_for(stream, device, tensors):
     one: tell the caching allocator they are in use on that stream, so that once the caller drops
     them their memory is not handed to a new allocation on the current stream while the call's
     kernels may still be reading or writing it."""
-    if not any(t is not None for t in tensors):
-        return
+    if stream is None or not any(t is not None for t in tensors):
+        return  # on the current stream itself, or nothing allocated here
     ts = _torch_stream(stream, device)
     if ts != torch.cuda.current_stream(device):
         for t in tensors:
@@ -355,27 +355,27 @@ class ChunkPlan:
         self.device = dev
         self.desc = _desc(T, N, Hk, Hv, self.workspace.data_ptr(), self.workspace.numel())
         self.args = (q, k, v, g, beta, cu_seqlens, h0)
+        # the plan's tensors keep their addresses: their pointer arguments are made once
+        self._desc_ref = ctypes.byref(self.desc)
+        pq, pk, pv, pg, pb, pcu, ph0 = (_ptr(t) for t in self.args)
+        self._prep_args = (pq, pk, pg, pb, pcu)
+        self._pass_args = (pq, pk, pv, pcu, ph0, _ptr(self.o), _ptr(self.hT))
+        self._fwd_args = (pq, pk, pv, pg, pb, pcu, ph0, _ptr(self.o), _ptr(self.hT))
 
     def prep(self, stream=None):
-        q, k, v, g, beta, cu, h0 = self.args
-        rc = lib().gdn_chunk_prep(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu),
-                                  _stream(stream, self.device))
+        rc = lib().gdn_chunk_prep(self._desc_ref, *self._prep_args, _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_chunk_prep")
         _keep_for(stream, self.device, self._fresh)
 
     def state_pass(self, stream=None):
-        q, k, v, g, beta, cu, h0 = self.args
-        rc = lib().gdn_state_pass(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(h0),
-                                  _ptr(self.o), _ptr(self.hT), _stream(stream, self.device))
+        rc = lib().gdn_state_pass(self._desc_ref, *self._pass_args, _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_state_pass")
         _keep_for(stream, self.device, self._fresh)
 
     def forward(self, stream=None):
-        q, k, v, g, beta, cu, h0 = self.args
-        rc = lib().gdn_chunk_fwd(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu),
-                                 _ptr(h0), _ptr(self.o), _ptr(self.hT), _stream(stream, self.device))
+        rc = lib().gdn_chunk_fwd(self._desc_ref, *self._fwd_args, _stream(stream, self.device))
         if rc != GDN_OK:
             raise GdnError(rc, "gdn_chunk_fwd")
         _keep_for(stream, self.device, self._fresh)
