@@ -45,6 +45,9 @@
  *  * The workspace is caller-owned device memory of at least *_workspace_size() bytes; its
  *    contents on entry are ignored and on exit are unspecified.  Calls that share a workspace
  *    must be ordered on one stream.
+ *  * The calls only launch kernels on `stream` (no allocation, no memset, no synchronisation), so
+ *    a caller may capture them in a HIP graph and replay it with new contents in the same buffers.
+ *    gdn_mixer_fwd_fused_norm, which launches cooperatively, is the exception.
  *  * Only dk = dv = 128 is supported (GDN_ERR_UNSUPPORTED otherwise).
  */
 #ifndef LIBGDN_GDN_H
