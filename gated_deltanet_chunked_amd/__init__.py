@@ -323,8 +323,10 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, h0=None, *, o, hT=None, 
 
 
 class ChunkPlan:
-    """Checked arguments of one gdn_chunk_fwd shape, for calling the two stages separately
-    (gdn_chunk_prep then gdn_state_pass) -- e.g. to time each kernel on its own."""
+    """Checked arguments of one gdn_chunk_fwd call on fixed buffers: forward() runs the whole call,
+    prep() and state_pass() its two stages (e.g. to time each kernel on its own).  The tensors are
+    bound when the plan is made (their pointers are kept); write new data into them between calls
+    rather than replacing them."""
 
     def __init__(self, q, k, v, g, beta, cu_seqlens, h0=None, *, o=None, hT=None, workspace=None,
                  cu_seqlens_host=None):
