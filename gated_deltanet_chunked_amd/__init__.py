@@ -16,6 +16,11 @@ Entry points (same names as the C ABI):
     gdn_mixer_fwd(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, ...) -> (y, hT)
     gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, ...)
         -> (y, hT, conv_out)
+    gdn_mixer_fwd_gates / gdn_mixer_fwd_gates_cont: the same with g and beta made from the
+        projections a, b and the per-head A_log, dt_bias
+    gdn_mixer_fwd_fused_norm: gdn_mixer_fwd with the gated RMSNorm inside the state pass
+ChunkPlan and MixerPlan check one call's arguments once, for repeated calls on fixed buffers
+(forward() then costs only the C call and its launches).
 
 Layouts (row-major, contiguous): q, k bf16 [T, Hk, 128]; v bf16 [T, Hv, 128]; g, beta fp32
 [T, Hv]; cu_seqlens int32 [N+1]; h0, hT fp32 [N, Hv, 128, 128] key-major (H = S^T); o bf16
@@ -428,8 +433,10 @@ def gdn_mixer_fwd_cont(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, con
                   conv_out, want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host)
 
 
-def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, cont, Hk, Hv, y, hT, conv_out,
-           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host, fused_norm=False, gates=None):
+def _mixer_call(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, cont, Hk, Hv, y, hT,
+                conv_out, want_state, want_window, norm_eps, workspace, cu_seqlens_host, fused_norm=False, gates=None):
+    """Checks a mixer call's arguments and allocates the outputs and workspace not given.  Returns
+    (C function, its name, its arguments but the stream, (y, hT, conv_out), tensors allocated)."""
     dev = qkv.device
     T = int(qkv.shape[0])
     C = (2 * Hk + Hv) * D
@@ -479,28 +486,58 @@ def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index
         raise GdnError(GDN_ERR_SHAPE, "gdn_mixer_fwd_workspace_size")
     workspace = _workspace(workspace, need, dev, fresh)
     m = MixerDesc(_desc(T, N, Hk, Hv, workspace.data_ptr(), workspace.numel()), 4, float(norm_eps))
+    ref = ctypes.byref(m)
     if cont and gates is not None:
-        rc = lib().gdn_mixer_fwd_gates_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(ga), _ptr(gb),
-                                            _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(cu_seqlens),
-                                            _ptr(h0), _ptr(conv_in), S, _ptr(state_index), _ptr(y), _ptr(hT),
-                                            _ptr(conv_out), _stream(stream, dev))
-        where = "gdn_mixer_fwd_gates_cont"
+        fn, where = lib().gdn_mixer_fwd_gates_cont, "gdn_mixer_fwd_gates_cont"
+        args = (ref, _ptr(qkv), _ptr(conv_w), _ptr(ga), _ptr(gb), _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w),
+                _ptr(cu_seqlens), _ptr(h0), _ptr(conv_in), S, _ptr(state_index), _ptr(y), _ptr(hT), _ptr(conv_out))
     elif cont:
-        rc = lib().gdn_mixer_fwd_cont(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z),
-                                      _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(conv_in), S, _ptr(state_index),
-                                      _ptr(y), _ptr(hT), _ptr(conv_out), _stream(stream, dev))
-        where = "gdn_mixer_fwd_cont"
+        fn, where = lib().gdn_mixer_fwd_cont, "gdn_mixer_fwd_cont"
+        args = (ref, _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0),
+                _ptr(conv_in), S, _ptr(state_index), _ptr(y), _ptr(hT), _ptr(conv_out))
     elif gates is not None:
-        rc = lib().gdn_mixer_fwd_gates(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(ga), _ptr(gb), _ptr(A_log),
-                                       _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0), _ptr(y),
-                                       _ptr(hT), _stream(stream, dev))
-        where = "gdn_mixer_fwd_gates"
+        fn, where = lib().gdn_mixer_fwd_gates, "gdn_mixer_fwd_gates"
+        args = (ref, _ptr(qkv), _ptr(conv_w), _ptr(ga), _ptr(gb), _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w),
+                _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT))
     else:
         fn, where = ((lib().gdn_mixer_fwd_fused_norm, "gdn_mixer_fwd_fused_norm") if fused_norm
                      else (lib().gdn_mixer_fwd, "gdn_mixer_fwd"))
-        rc = fn(ctypes.byref(m), _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
-                _ptr(cu_seqlens), _ptr(h0), _ptr(y), _ptr(hT), _stream(stream, dev))
+        args = (ref, _ptr(qkv), _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w), _ptr(cu_seqlens), _ptr(h0),
+                _ptr(y), _ptr(hT))
+    return fn, where, args, (y, hT, conv_out), fresh
+
+
+def _mixer(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index, cont, Hk, Hv, y, hT, conv_out,
+           want_state, want_window, norm_eps, workspace, stream, cu_seqlens_host, fused_norm=False, gates=None):
+    fn, where, args, outs, fresh = _mixer_call(qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, conv_in, state_index,
+                                               cont, Hk, Hv, y, hT, conv_out, want_state, want_window, norm_eps,
+                                               workspace, cu_seqlens_host, fused_norm, gates)
+    dev = qkv.device
+    rc = fn(*args, _stream(stream, dev))
     if rc != GDN_OK:
         raise GdnError(rc, where)
     _keep_for(stream, dev, fresh)
-    return y, hT, conv_out
+    return outs
+
+
+class MixerPlan:
+    """Checked arguments of one gdn_mixer_fwd call on fixed buffers (gdn_mixer_fwd_gates with
+    gates=(a, b, A_log, dt_bias), g and beta then None); forward() runs it and returns (y, hT).
+    The tensors are bound when the plan is made (their pointers are kept); write new data into
+    them between calls rather than replacing them."""
+
+    def __init__(self, qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0=None, *, Hk=16, Hv=32, y=None, hT=None,
+                 want_state=True, norm_eps=1e-6, workspace=None, cu_seqlens_host=None, gates=None):
+        self.device = qkv.device
+        self._fn, self._where, self._args, outs, self._fresh = _mixer_call(
+            qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, None, None, False, Hk, Hv, y, hT, None, want_state,
+            False, norm_eps, workspace, cu_seqlens_host, False, gates)
+        self.y, self.hT, _ = outs
+        self._keep = (qkv, conv_w, g, beta, z, norm_w, cu_seqlens, h0, gates, workspace)
+
+    def forward(self, stream=None):
+        rc = self._fn(*self._args, _stream(stream, self.device))
+        if rc != GDN_OK:
+            raise GdnError(rc, self._where)
+        _keep_for(stream, self.device, self._fresh)
+        return self.y, self.hT

@@ -183,3 +183,36 @@ def test_mixer_gates(case):
     hT = hT.cpu().numpy().astype(np.float64)
     mg = dataclasses.replace(m, g=g, beta=beta)
     check_mixer(y, hT, *run_mixer_oracle(mg, Hk, Hv), f"gates {case}", mg)
+
+
+@pytest.mark.parametrize("form", ["plain", "gates"])
+def test_mixer_plan(form):
+    # MixerPlan checks the arguments once; forward() on new data written into its buffers equals
+    # gdn_mixer_fwd (or gdn_mixer_fwd_gates) on the same data, bit for bit, call after call.
+    T, Hk, Hv = gi.MIXER_T, 16, 32
+    say(f"[mixer-plan] {form} T={T}")
+    m = gi.make_mixer_inputs(120)
+    t = dict(qkv=bf16_dev(m.qkv), conv_w=bf16_dev(m.conv_w), g=f32_dev(m.g), beta=f32_dev(m.beta), z=bf16_dev(m.z),
+             norm_w=bf16_dev(m.norm_w), cu=torch.from_numpy(m.cu.astype(np.int32)).cuda())
+    cu_h = torch.from_numpy(m.cu.astype(np.int64))
+    gates = None
+    if form == "gates":
+        gt = gi.make_gate_inputs(121, T, Hv)
+        gates = (bf16_dev(gt.a), bf16_dev(gt.b), f32_dev(gt.A_log), f32_dev(gt.dt_bias))
+    plan = gdn.MixerPlan(t["qkv"], t["conv_w"], None if gates else t["g"], None if gates else t["beta"], t["z"],
+                         t["norm_w"], t["cu"], None, Hk=Hk, Hv=Hv, cu_seqlens_host=cu_h, gates=gates)
+    for rep in range(3):
+        m2 = gi.make_mixer_inputs(130 + rep)
+        t["qkv"].copy_(bf16_dev(m2.qkv))
+        t["z"].copy_(bf16_dev(m2.z))
+        y_p, h_p = plan.forward()
+        if gates:
+            y_e, h_e = gdn.gdn_mixer_fwd_gates(t["qkv"], t["conv_w"], *gates, t["z"], t["norm_w"], t["cu"], None,
+                                               Hk=Hk, Hv=Hv, cu_seqlens_host=cu_h)
+        else:
+            y_e, h_e = gdn.gdn_mixer_fwd(t["qkv"], t["conv_w"], t["g"], t["beta"], t["z"], t["norm_w"], t["cu"], None,
+                                         Hk=Hk, Hv=Hv, cu_seqlens_host=cu_h)
+        torch.cuda.synchronize()
+        assert torch.equal(y_p.view(torch.int16), y_e.view(torch.int16)), f"call {rep}: y differs"
+        assert torch.equal(h_p, h_e), f"call {rep}: hT differs"
+    say("  3 plan calls bitwise equal to the function")
