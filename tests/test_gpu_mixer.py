@@ -216,3 +216,35 @@ def test_mixer_plan(form):
         assert torch.equal(y_p.view(torch.int16), y_e.view(torch.int16)), f"call {rep}: y differs"
         assert torch.equal(h_p, h_e), f"call {rep}: hT differs"
     say("  3 plan calls bitwise equal to the function")
+
+
+def test_mixer_side_stream_with_binding_allocations():
+    # The binding allocates y, hT and the workspace itself; the calls run on a side stream while the
+    # current stream keeps allocating and writing memory of the same sizes.  The allocations are
+    # recorded on the side stream, so none of that memory may be reused under the calls.  Also
+    # want_state=False: no state returned, the same y.
+    T, Hk, Hv = gi.MIXER_T, 16, 32
+    say(f"[mixer-side-stream] T={T} on a side stream, allocations on the current stream")
+    m = gi.make_mixer_inputs(140)
+    args = (bf16_dev(m.qkv), bf16_dev(m.conv_w), f32_dev(m.g), f32_dev(m.beta), bf16_dev(m.z), bf16_dev(m.norm_w),
+            torch.from_numpy(m.cu.astype(np.int32)).cuda(), None)
+    cu_h = torch.from_numpy(m.cu.astype(np.int64))
+    y_ref, h_ref = gdn.gdn_mixer_fwd(*args, Hk=Hk, Hv=Hv, cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    ws_n = gdn.gdn_mixer_fwd_workspace_size(T, 1, Hk, Hv)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(gdn.gdn_mixer_fwd(*args, Hk=Hk, Hv=Hv, stream=side, cu_seqlens_host=cu_h))
+        junk = [torch.full((ws_n,), 0xFF, dtype=torch.uint8, device="cuda"),
+                torch.full((T, Hv, 128), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                torch.full((1, Hv, 128, 128), float("nan"), dtype=torch.float32, device="cuda")]
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    y_ns, h_ns = gdn.gdn_mixer_fwd(*args, Hk=Hk, Hv=Hv, want_state=False, cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    for y, hT in outs:
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)) and torch.equal(hT, h_ref)
+    assert h_ns is None and torch.equal(y_ns.view(torch.int16), y_ref.view(torch.int16))
+    say("  3 side-stream calls and a call without state bitwise equal to the current-stream call")
