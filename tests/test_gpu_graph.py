@@ -104,3 +104,36 @@ def test_graph_replay_mixer_layers():
             assert torch.equal(y_g.view(torch.int16), y_e.view(torch.int16)), f"replay {rep} layer {l}: y differs"
             assert torch.equal(h_g, h_e), f"replay {rep} layer {l}: hT differs"
     say("  3 replays of two layers bitwise equal to eager calls")
+
+
+def test_graph_replay_mixer_plan_gates():
+    # a MixerPlan with the gates made in the first kernel and an initial state, captured once
+    T, Hk, Hv = gi.MIXER_T, 16, 32
+    say(f"[graph] MixerPlan with gates and h0, T={T}")
+    m = gi.make_mixer_inputs(820, with_h0=True)
+    gt = gi.make_gate_inputs(821, T, Hv)
+    t = dict(qkv=bf16_dev(m.qkv), conv_w=bf16_dev(m.conv_w), z=bf16_dev(m.z), norm_w=bf16_dev(m.norm_w),
+             cu=torch.from_numpy(m.cu.astype(np.int32)).cuda(), h0=f32_dev(m.h0))
+    gates = (bf16_dev(gt.a), bf16_dev(gt.b), f32_dev(gt.A_log), f32_dev(gt.dt_bias))
+    cu_h = torch.from_numpy(m.cu.astype(np.int64))
+    plan = gdn.MixerPlan(t["qkv"], t["conv_w"], None, None, t["z"], t["norm_w"], t["cu"], t["h0"], Hk=Hk, Hv=Hv,
+                         cu_seqlens_host=cu_h, gates=gates)
+    graph = _capture(plan.forward)
+    for rep in range(3):
+        m2 = gi.make_mixer_inputs(830 + rep, with_h0=True)
+        g2 = gi.make_gate_inputs(840 + rep, T, Hv)
+        t["qkv"].copy_(bf16_dev(m2.qkv))
+        t["z"].copy_(bf16_dev(m2.z))
+        t["h0"].copy_(f32_dev(m2.h0))
+        gates[0].copy_(bf16_dev(g2.a))
+        gates[1].copy_(bf16_dev(g2.b))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_g, h_g = plan.y.clone(), plan.hT.clone()
+        y_e, h_e = gdn.gdn_mixer_fwd_gates(t["qkv"], t["conv_w"], *gates, t["z"], t["norm_w"], t["cu"], t["h0"],
+                                           Hk=Hk, Hv=Hv, cu_seqlens_host=cu_h)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int16), y_e.view(torch.int16)), f"replay {rep}: y differs"
+        assert torch.equal(h_g, h_e), f"replay {rep}: hT differs"
+    say("  3 replays bitwise equal to eager calls")
