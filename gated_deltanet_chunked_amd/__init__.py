@@ -358,6 +358,8 @@ class ChunkPlan:
         _check(self.o, "o", torch.bfloat16, (T, Hv, D), dev)
         _check(self.hT, "hT", torch.float32, (N, Hv, D, D), dev)
         need = gdn_chunk_fwd_workspace_size(T, N, Hk, Hv)
+        if need == 0:
+            raise GdnError(GDN_ERR_SHAPE, "gdn_chunk_fwd_workspace_size")
         self.workspace = _workspace(workspace, need, dev, self._fresh)
         self.device = dev
         self.desc = _desc(T, N, Hk, Hv, self.workspace.data_ptr(), self.workspace.numel())

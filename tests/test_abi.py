@@ -350,3 +350,67 @@ def test_binding_cu_seqlens_host_check():
     for host in bad:
         with pytest.raises(ValueError):
             gdn._check_cu(None, T, host)
+
+
+def test_plan_argument_checks():
+    # ChunkPlan and MixerPlan check every argument on the host when they are made; nothing is
+    # launched here (forward() is never called).  Valid arguments give outputs of the right shapes;
+    # each kind of mistake raises.  The tensors are CPU tensors: the checks only ask that all of a
+    # call's tensors share one device.
+    import torch
+
+    T, Hk, Hv, D = 100, 2, 4, 128
+    bf, f32 = torch.bfloat16, torch.float32
+    cu_h = [0, 40, T]
+    c = dict(q=torch.zeros((T, Hk, D), dtype=bf), k=torch.zeros((T, Hk, D), dtype=bf),
+             v=torch.zeros((T, Hv, D), dtype=bf), g=torch.zeros((T, Hv), dtype=f32),
+             beta=torch.zeros((T, Hv), dtype=f32), cu_seqlens=torch.tensor(cu_h, dtype=torch.int32))
+
+    def chunk(**kw):
+        a = dict(c, **kw)
+        host = a.pop("cu_seqlens_host", cu_h)
+        return gdn.ChunkPlan(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu_seqlens"], a.get("h0"),
+                             workspace=a.get("workspace"), cu_seqlens_host=host)
+
+    p = chunk()
+    assert p.o.shape == (T, Hv, D) and p.o.dtype == bf and p.hT.shape == (2, Hv, D, D)
+    assert p.workspace.numel() == gdn.gdn_chunk_fwd_workspace_size(T, 2, Hk, Hv)
+    bad = [(TypeError, dict(g=c["g"].double())),
+           (ValueError, dict(beta=c["beta"][:-1])),
+           (ValueError, dict(v=torch.zeros((T, Hv, 2 * D), dtype=bf)[..., :D])),  # not contiguous
+           (ValueError, dict(h0=torch.zeros((1, Hv, D, D), dtype=f32))),  # one state for two sequences
+           (TypeError, dict(cu_seqlens=c["cu_seqlens"].long())),
+           (ValueError, dict(cu_seqlens_host=[0, 60, 40, T])),
+           (ValueError, dict(workspace=torch.zeros(16, dtype=torch.uint8))),
+           (gdn.GdnError, dict(v=torch.zeros((T, 3, D), dtype=bf), g=torch.zeros((T, 3), dtype=f32),
+                               beta=torch.zeros((T, 3), dtype=f32)))]  # Hv not a multiple of Hk
+    for exc, kw in bad:
+        with pytest.raises(exc):
+            chunk(**kw)
+
+    C = (2 * Hk + Hv) * D
+    m = dict(qkv=torch.zeros((T, C), dtype=bf), conv_w=torch.zeros((C, 4), dtype=bf), g=c["g"], beta=c["beta"],
+             z=torch.zeros((T, Hv, D), dtype=bf), norm_w=torch.ones(D, dtype=bf), cu_seqlens=c["cu_seqlens"])
+
+    def mixer(gates=None, want_state=True, **kw):
+        a = dict(m, **kw)
+        return gdn.MixerPlan(a["qkv"], a["conv_w"], a["g"], a["beta"], a["z"], a["norm_w"], a["cu_seqlens"],
+                             a.get("h0"), Hk=a.get("Hk", Hk), Hv=Hv, want_state=want_state, cu_seqlens_host=cu_h,
+                             gates=gates)
+
+    p = mixer()
+    assert p.y.shape == (T, Hv, D) and p.hT.shape == (2, Hv, D, D)
+    assert mixer(want_state=False).hT is None
+    gates = (torch.zeros((T, Hv), dtype=bf), torch.zeros((T, Hv), dtype=bf), torch.zeros(Hv, dtype=f32),
+             torch.zeros(Hv, dtype=f32))
+    assert mixer(gates=gates, g=None, beta=None).y.shape == (T, Hv, D)
+    bad = [(ValueError, dict(qkv=torch.zeros((T, C - D), dtype=bf))),
+           (TypeError, dict(z=torch.zeros((T, Hv, D), dtype=f32))),
+           (ValueError, dict(conv_w=torch.zeros((C, 3), dtype=bf))),
+           (ValueError, dict(h0=torch.zeros((2, Hv, D, 64), dtype=f32))),
+           (TypeError, dict(gates=(gates[0].float(),) + gates[1:], g=None, beta=None)),
+           (ValueError, dict(gates=gates[:2] + (torch.zeros(Hv + 1, dtype=f32), gates[3]), g=None, beta=None)),
+           (ValueError, dict(Hk=3))]  # qkv's width no longer matches (2 Hk + Hv) 128
+    for exc, kw in bad:
+        with pytest.raises(exc):
+            mixer(**kw)
