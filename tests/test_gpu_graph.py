@@ -137,3 +137,44 @@ def test_graph_replay_mixer_plan_gates():
         assert torch.equal(y_g.view(torch.int16), y_e.view(torch.int16)), f"replay {rep}: y differs"
         assert torch.equal(h_g, h_e), f"replay {rep}: hT differs"
     say("  3 replays bitwise equal to eager calls")
+
+
+def test_graph_replay_mixer_cont_in_place():
+    # A prefill taken piece by piece from a captured graph: one gdn_mixer_fwd_cont call whose state
+    # and conv window pools are updated in place (hT = h0, conv_out = conv_in), so every replay
+    # continues from the previous one.  Each replay equals the same call made eagerly on pools that
+    # went through the same pieces.
+    Hk, Hv, D, lengths = 2, 4, 128, [64, 37]
+    say(f"[graph] gdn_mixer_fwd_cont in place, pieces of lengths {lengths}")
+    m = gi.make_mixer_inputs(850, lengths=lengths, Hk=Hk, Hv=Hv)
+    C, T = m.qkv.shape[1], int(m.cu[-1])
+    t = dict(qkv=bf16_dev(m.qkv), conv_w=bf16_dev(m.conv_w), g=f32_dev(m.g), beta=f32_dev(m.beta), z=bf16_dev(m.z),
+             norm_w=bf16_dev(m.norm_w), cu=torch.from_numpy(m.cu.astype(np.int32)).cuda())
+    cu_h = torch.from_numpy(m.cu.astype(np.int64))
+    h_pool, w_pool = f32_dev(gi.make_state_pool(851, 2, Hv)), bf16_dev(gi.make_window_pool(852, 2, C))
+    h_eager, w_eager = h_pool.clone(), w_pool.clone()
+    y = torch.empty((T, Hv, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.gdn_mixer_fwd_workspace_size(T, 2, Hk, Hv), dtype=torch.uint8, device="cuda")
+
+    def call(h, w, out):
+        return gdn.gdn_mixer_fwd_cont(t["qkv"], t["conv_w"], t["g"], t["beta"], t["z"], t["norm_w"], t["cu"], h, w,
+                                      Hk=Hk, Hv=Hv, y=out, hT=h, conv_out=w, workspace=ws, cu_seqlens_host=cu_h)
+
+    h_start, w_start = h_pool.clone(), w_pool.clone()
+    graph = _capture(lambda: call(h_pool, w_pool, y))
+    h_pool.copy_(h_start)  # the warm-up and the capture may have advanced the pools
+    w_pool.copy_(w_start)
+    for rep in range(4):
+        p = gi.make_mixer_inputs(860 + rep, lengths=lengths, Hk=Hk, Hv=Hv)
+        for key, val in (("qkv", bf16_dev(p.qkv)), ("g", f32_dev(p.g)), ("beta", f32_dev(p.beta)), ("z", bf16_dev(p.z))):
+            t[key].copy_(val)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_g = y.clone()
+        y_e, _, _ = call(h_eager, w_eager, None)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int16), y_e.view(torch.int16)), f"piece {rep}: y differs"
+        assert torch.equal(h_pool, h_eager), f"piece {rep}: state pool differs"
+        assert torch.equal(w_pool.view(torch.int16), w_eager.view(torch.int16)), f"piece {rep}: window pool differs"
+    say("  4 pieces replayed, each bitwise equal to the eager continuation")
